@@ -1,0 +1,335 @@
+"""Throughput of the block-scaled FP4 quantize-dequantize path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over the fp32 4096 x 4096
+block-size-sweep workload (the numerical study of "Finer is Better (with the
+Right Scaling)": N(0,1) and Laplace(0,1) tensors, each also scaled by 1e-4):
+  * 128 fp4q_quantize calls: 4 tensors x block {4, 8, 16, 32} x
+    {abs-max, prevent-zero, 4-over-6, brute force} x {tensor-amax, none},
+    every output (packed codes, E4M3 scales, fp32 dequant, block MSE);
+  * block-wise Hadamard rotation fused into quantization (H = 16 NVFP4,
+    H = 32 MXFP4) on the N(0,1) tensor;
+  * FOCUS relaxed fake-quant forward (+ codes) and STE backward on the
+    N(0,1) tensor (MXFP4 and NVFP4, sub-blocks of 8, fp16 c ~ U[0.8, 1.25],
+    upstream gradient N(0,1));
+  * stand-alone dequantize and block MSE of one NVFP4 result.
+Calls cycle through the four tensors so consecutive calls touch different
+256 MB of data (the 256 MB last-level cache cannot serve a whole tensor from
+one call to the next).
+
+All inputs are generated once and are resident in HBM before timing; every
+output buffer is preallocated; the timed region holds only library calls.
+value = algorithmic bytes of the step (each input read once, each output
+written once) / step time.  Per-call HIP events over the timed steps give
+the per-strategy rates and the roofline of the dominant kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, published
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # 256 CUs x 64 lanes x 2.4 GHz, one op per lane per clock
+BF_OPS_PER_EVAL = 13                       # VALU ops of one exact candidate-element evaluation (see design notes)
+
+STRATS = {0: "absmax", 1: "prevent-zero", 2: "4-over-6", 3: "brute-force"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=12, help="rows per tensor in the oracle sample")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+class Call:
+    """One preallocated library call of the step."""
+
+    def __init__(self, name, fn, args, nbytes, elems, kind, meta):
+        self.name, self.fn, self.args = name, fn, args
+        self.nbytes, self.elems, self.kind, self.meta = nbytes, elems, kind, meta
+        self.times = []
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"{self.name}: status {st}")
+
+
+def quant_bytes(rows, cols, B, in_es=4, dq_es=4, mse=True, dq=True):
+    n = rows * cols
+    return n * in_es + n // 2 + n // B + (n * dq_es if dq else 0) + (4 * n // B if mse else 0)
+
+
+def build_step(F, S, torch, dev):
+    """Generate the workload on the host, upload it, preallocate every output."""
+    L = F.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    host = S.config2()
+    names = ["normal", "laplace", "normal_1e-4", "laplace_1e-4"]
+    R, C = host["normal"].shape
+    X = {k: S.to_torch(host[k], S.F32, dev) for k in names}
+    keep = []                                    # keep tensors and configs alive
+
+    def t_empty(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=dev)
+        keep.append(t)
+        return t
+
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+    calls = []
+    combos = [(B, st, gm) for B in (4, 8, 16, 32) for st in (0, 1, 2, 3) for gm in (1, 0)]
+    i = 0
+    for B, st, gm in combos:
+        for name in names:
+            x = X[names[(names.index(name) + i) % 4]]
+            i += 1
+            cfg = F.config(F.E4M3, B, st, gm)
+            keep.append(cfg)
+            codes = t_empty((R, C // 2), torch.uint8)
+            scales = t_empty((R, C // B), torch.uint8)
+            g = t_empty((1,), torch.float32)
+            dq = t_empty((R, C), torch.float32)
+            mse = t_empty((R, C // B), torch.float32)
+            ws = t_empty((max(F.workspace_bytes(cfg, R, C), 16),), torch.uint8)
+            args = (ctypes.byref(cfg), ptr(x), F.F32, R, C, C, ptr(codes), ptr(scales), ptr(g), ptr(dq),
+                    F.F32, C, ptr(mse), ptr(ws), stream)
+            calls.append(Call(f"quantize B={B} {STRATS[st]} {'amax' if gm else 'none'}", L.fp4q_quantize, args,
+                              quant_bytes(R, C, B), R * C, "quantize",
+                              dict(B=B, strategy=STRATS[st], global_mode="tensor-amax" if gm else "none")))
+
+    xn = X["normal"]
+    # block Hadamard fused before quantization
+    for H, cfg in ((16, F.nvfp4(0, hadamard=16)), (32, F.mxfp4(0, hadamard=32))):
+        keep.append(cfg)
+        codes = t_empty((R, C // 2), torch.uint8)
+        scales = t_empty((R, C // cfg.block), torch.uint8)
+        g = t_empty((1,), torch.float32)
+        dq = t_empty((R, C), torch.float32)
+        mse = t_empty((R, C // cfg.block), torch.float32)
+        ws = t_empty((max(F.workspace_bytes(cfg, R, C), 16),), torch.uint8)
+        args = (ctypes.byref(cfg), ptr(xn), F.F32, R, C, C, ptr(codes), ptr(scales), ptr(g), ptr(dq), F.F32, C,
+                ptr(mse), ptr(ws), stream)
+        calls.append(Call(f"quantize hadamard={H} {'nvfp4' if H == 16 else 'mxfp4'}", L.fp4q_quantize, args,
+                          quant_bytes(R, C, cfg.block), R * C, "rotate+quantize", dict(H=H)))
+        if H == 16:
+            nv_codes, nv_scales, nv_g, nv_cfg = codes, scales, g, cfg
+
+    # stand-alone dequantize and block MSE of the NVFP4 (rotated) result
+    out = t_empty((R, C), torch.float32)
+    calls.append(Call("dequantize nvfp4", L.fp4q_dequantize,
+                      (ctypes.byref(nv_cfg), ptr(nv_codes), ptr(nv_scales), ptr(nv_g), R, C, ptr(out), F.F32, C, stream),
+                      R * C // 2 + R * C // 16 + 4 * R * C, R * C, "dequantize", {}))
+    mse = t_empty((R, C // 16), torch.float32)
+    calls.append(Call("block_mse nvfp4", L.fp4q_block_mse,
+                      (ctypes.byref(nv_cfg), ptr(xn), F.F32, R, C, C, ptr(nv_codes), ptr(nv_scales), ptr(nv_g),
+                       ptr(mse), stream),
+                      4 * R * C + R * C // 2 + R * C // 16 + 4 * R * C // 16, R * C, "block_mse", {}))
+
+    # FOCUS relaxed fake-quant forward / backward, sub-blocks of 8
+    K = 8
+    rng = np.random.default_rng(7)
+    c16 = S.cast(rng.uniform(0.8, 1.25, (R, C // K)), S.F16)
+    ct = S.to_torch(c16, S.F16, dev)
+    gt = S.to_torch(S.normal(R, C, 8, S.F32), S.F32, dev)
+    keep += [ct, gt]
+    for cfg in (F.mxfp4(), F.nvfp4(0, F.GLOBAL_USER, 2.0 ** -12)):
+        keep.append(cfg)
+        B = cfg.block
+        scales = t_empty((R, C // B), torch.uint8)
+        gq = t_empty((1,), torch.float32)
+        codes = t_empty((R, C // 2), torch.uint8)
+        ws = t_empty((16,), torch.uint8)
+        # S_dq from abs-max quantization (outside the timed step)
+        st = L.fp4q_quantize(ctypes.byref(cfg), ptr(xn), F.F32, R, C, C, ptr(codes), ptr(scales), ptr(gq),
+                             None, F.F32, C, None, ptr(ws), stream)
+        assert st == 0, st
+        g_in = None if cfg.scale_fmt == F.E8M0 else gq
+        w_hat = t_empty((R, C), torch.float32)
+        fcodes = t_empty((R, C // 2), torch.uint8)
+        grad_c = t_empty((R, C // K), torch.float32)
+        fmt = "mxfp4" if B == 32 else "nvfp4"
+        calls.append(Call(f"focus fwd {fmt}", L.fp4q_relaxed_fakequant_fwd,
+                          (ctypes.byref(cfg), ptr(xn), F.F32, R, C, C, ptr(scales), ptr(g_in), ptr(ct), K,
+                           ptr(w_hat), F.F32, C, ptr(fcodes), stream),
+                          4 * R * C + 2 * R * C // K + R * C // B + 4 * R * C + R * C // 2, R * C, "focus_fwd", {}))
+        calls.append(Call(f"focus bwd {fmt}", L.fp4q_relaxed_fakequant_bwd,
+                          (ctypes.byref(cfg), ptr(xn), F.F32, R, C, C, ptr(scales), ptr(g_in), ptr(ct), K, ptr(gt),
+                           F.F32, C, ptr(grad_c), stream),
+                          8 * R * C + 2 * R * C // K + R * C // B + 4 * R * C // K, R * C, "focus_bwd", {}))
+    torch.cuda.synchronize()
+    return calls, keep, host
+
+
+def cpu_baseline(O, S, host, rows_per_tensor):
+    """The oracle (single thread) on the first rows of every tensor, over the
+    same call list as one GPU step."""
+    names = ["normal", "laplace", "normal_1e-4", "laplace_1e-4"]
+    nbytes = 0
+    t0 = time.perf_counter()
+    for B in (4, 8, 16, 32):
+        for st in (0, 1, 2, 3):
+            for gm in (1, 0):
+                for name in names:
+                    x = np.ascontiguousarray(host[name][:rows_per_tensor])
+                    O.quantize(x, fmt=1, block=B, strategy=st, global_mode=gm)
+                    nbytes += quant_bytes(x.shape[0], x.shape[1], B)
+    x = np.ascontiguousarray(host["normal"][:rows_per_tensor])
+    r, c = x.shape
+    for H, fmt, B, gm in ((16, 1, 16, 1), (32, 0, 32, 0)):
+        q = O.quantize(x, fmt=fmt, block=B, strategy=0, global_mode=gm, hadamard=H)
+        nbytes += quant_bytes(r, c, B)
+    O.dequantize(q["codes"], q["scales"], 1.0, fmt=0, block=32, rows=r, cols=c)
+    nbytes += r * c // 2 + r * c // 32 + 4 * r * c
+    O.block_mse(x, q["codes"], q["scales"], 1.0, fmt=0, block=32, hadamard=32)
+    nbytes += 4 * r * c + r * c // 2 + r * c // 32 + 4 * r * c // 32
+    c16 = S.cast(np.random.default_rng(7).uniform(0.8, 1.25, (r, c // 8)), S.F16)
+    gr = S.normal(r, c, 8, S.F32)
+    for fmt, B, g in ((0, 32, 1.0), (1, 16, 2.0 ** -12)):
+        q = O.quantize(x, fmt=fmt, block=B, strategy=0, global_mode=2 if fmt else 0, user_g=g, dq_dt=None)
+        O.relaxed_fwd(x, q["scales"], g, c16, fmt=fmt, block=B, sub_block=8)
+        O.relaxed_bwd(x, q["scales"], g, c16, gr, fmt=fmt, block=B, sub_block=8)
+        nbytes += 8 * r * c + r * c // 4 + r * c // B + r * c // 2
+        nbytes += 8 * r * c + r * c // 4 + r * c // B + r * c // 2
+    dt = time.perf_counter() - t0
+    return nbytes, dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no multi-GPU "
+              "code: each GPU would quantize its own row shard independently).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from microscaling_fp4_block_fp4q_amd import fp4q as F
+    from microscaling_fp4_block_fp4q_amd import synth as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating and uploading the workload", file=sys.stderr, flush=True)
+    calls, keep, host = build_step(F, S, torch, dev)
+    step_bytes = sum(c.nbytes for c in calls)
+
+    def step(record=False):
+        for c in calls:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                c()
+                e1.record()
+                c.times.append((e0, e1))
+            else:
+                c()
+
+    print(f"[bench] {len(calls)} calls per step, warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps bracketed by device synchronisation
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    per_call = []
+    for c in calls:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in c.times]))
+        per_call.append((c, ms))
+
+    # per-strategy aggregates (quantize calls)
+    groups = {}
+    for c, ms in per_call:
+        key = c.meta.get("strategy", c.kind)
+        g = groups.setdefault(key, [0, 0, 0.0])
+        g[0] += c.nbytes
+        g[1] += c.elems
+        g[2] += ms
+    breakdown = {k: {"GB/s": round(b / (ms * 1e6), 1), "Gelem/s": round(e / (ms * 1e6), 2),
+                     "hbm_frac": round(b / (ms * 1e6) / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4)}
+                 for k, (b, e, ms) in groups.items()}
+
+    # dominant kernel: the call family with the largest share of the step
+    bf = [(c, ms) for c, ms in per_call if c.meta.get("strategy") == "brute-force" and c.meta.get("global_mode") == "none"]
+    bf16 = [(c, ms) for c, ms in bf if c.meta["B"] == 16]
+    dom, dom_ms = bf16[0]
+    evals = 126 * dom.elems
+    achieved_tops = evals * BF_OPS_PER_EVAL / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "alu", "kernel": "k_quant<float, B=16, H=0, E4M3, BRUTE_FORCE>",
+                "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s",
+                "frac": round(achieved_tops / VALU_PEAK_TOPS, 4), "traffic": None,
+                "avg_launch_ms": round(dom_ms, 4),
+                "work_per_launch": f"{evals} candidate-element evaluations x {BF_OPS_PER_EVAL} VALU ops"}
+    stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
+    sb = sum(c.nbytes for c, _ in stream_quant)
+    sms = sum(ms for _, ms in stream_quant)
+
+    result = {
+        "metric": "FP4 quantize+dequant GB/s and Gelem/s per strategy; % of HBM/VALU peak",
+        "value": round(step_bytes / (ms_per_step * 1e6), 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "fp32 4096x4096 N(0,1) and Laplace(0,1), each also x1e-4; E4M3-scaled FP4, "
+                               "block 4/8/16/32 x {abs-max, prevent-zero, 4-over-6, brute-force} x "
+                               "{tensor-amax, none}, all outputs; + block-Hadamard 16/32 fused quantize, "
+                               "FOCUS fwd/bwd (sub-block 8), dequantize, block MSE",
+                   "calls_per_step": len(calls), "algorithmic_bytes_per_step": step_bytes},
+        "roofline": roofline,
+        "streaming_absmax_4over6": {"GB/s": round(sb / (sms * 1e6), 1),
+                                    "hbm_frac": round(sb / (sms * 1e6) / HBM_PEAK_GBS, 4)},
+        "per_strategy": breakdown,
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        O.build()
+        print(f"[bench] oracle on {args.cpu_rows} rows per tensor (1 thread)", file=sys.stderr, flush=True)
+        nb, dt = cpu_baseline(O, S, host, args.cpu_rows)
+        result["cpu_baseline"] = {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the step's call list on the first {args.cpu_rows} rows of each "
+                                            f"4096x4096 tensor ({nb / 1e6:.1f} MB algorithmic, {dt:.1f} s)"}
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    per = sorted(per_call, key=lambda t: -t[1])
+    for c, ms in per[:12]:
+        print(f"[bench] {c.name:40s} {ms:9.4f} ms  {c.nbytes / (ms * 1e6):8.1f} GB/s", file=sys.stderr)
+
+
+if __name__ == "__main__":
+    main()

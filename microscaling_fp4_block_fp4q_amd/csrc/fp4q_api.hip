@@ -1,0 +1,331 @@
+// fp4q_api.hip -- the C ABI of include/fp4q.h: synchronous argument
+// validation on the host, then kernel launches on the caller's stream.
+// Nothing here allocates, synchronises or keeps state.
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fp4q.h"
+#include "fp4q_launch.hpp"
+
+using namespace fp4q_dev;
+
+namespace {
+
+constexpr int kMaxGrid = 2048;   // workgroups of a grid-stride launch
+
+int elem_size(int dt) { return dt == FP4Q_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == FP4Q_F32 || dt == FP4Q_BF16 || dt == FP4Q_F16; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int grid_for(int64_t units) {
+    int64_t g = (units + kThreads - 1) / kThreads;
+    if (g < 1) g = 1;
+    return (int)(g < kMaxGrid ? g : kMaxGrid);
+}
+
+// Checks of the configuration shared by every call.
+fp4q_status check_config(const fp4q_config* cfg) {
+    if (!cfg || cfg->struct_size != sizeof(fp4q_config)) return FP4Q_ERR_INVALID_ARG;
+    if (cfg->scale_fmt != FP4Q_SCALE_E8M0 && cfg->scale_fmt != FP4Q_SCALE_E4M3) return FP4Q_ERR_INVALID_ARG;
+    if (cfg->strategy < FP4Q_ABSMAX || cfg->strategy > FP4Q_GIVEN) return FP4Q_ERR_INVALID_ARG;
+    if (cfg->global_mode < FP4Q_GLOBAL_NONE || cfg->global_mode > FP4Q_GLOBAL_USER) return FP4Q_ERR_INVALID_ARG;
+    if (cfg->hadamard < 0) return FP4Q_ERR_INVALID_ARG;
+    if (cfg->block != 4 && cfg->block != 8 && cfg->block != 16 && cfg->block != 32) return FP4Q_ERR_SHAPE;
+    if (cfg->hadamard != 0 && cfg->hadamard != 16 && cfg->hadamard != 32) return FP4Q_ERR_UNSUPPORTED;
+    if (cfg->scale_fmt == FP4Q_SCALE_E8M0 &&
+        (cfg->global_mode != FP4Q_GLOBAL_NONE || cfg->strategy == FP4Q_FOUR_OVER_SIX))
+        return FP4Q_ERR_UNSUPPORTED;
+    if (cfg->global_mode == FP4Q_GLOBAL_USER) {
+        const double g = cfg->global_scale;
+        if (!(g >= FLT_MIN) || !(448.0 * g < FLT_MAX)) return FP4Q_ERR_INVALID_ARG;
+    }
+    return FP4Q_OK;
+}
+
+// A [rows, ld] tensor operand of element type dt.
+fp4q_status check_tensor(const void* p, int dt, int64_t rows, int64_t cols, int64_t ld) {
+    if (!p) return FP4Q_ERR_INVALID_ARG;
+    if (!dtype_ok(dt)) return FP4Q_ERR_INVALID_ARG;
+    if (ld < cols) return FP4Q_ERR_SHAPE;
+    (void)rows;
+    const int es = elem_size(dt);
+    if (!aligned16(p) || (ld * es) % 16 != 0 || (cols * es) % 16 != 0) return FP4Q_ERR_ALIGNMENT;
+    return FP4Q_OK;
+}
+
+fp4q_status check_dims(int64_t rows, int64_t cols, int block, int H) {
+    if (rows < 0 || cols < 0) return FP4Q_ERR_INVALID_ARG;
+    if (cols > 0 && rows > INT64_MAX / 64 / cols) return FP4Q_ERR_INVALID_ARG;
+    if (cols % block != 0) return FP4Q_ERR_SHAPE;
+    if (H && cols % H != 0) return FP4Q_ERR_SHAPE;
+    return FP4Q_OK;
+}
+
+fp4q_status check_buffer(const void* p) {
+    if (!p) return FP4Q_ERR_INVALID_ARG;
+    return aligned16(p) ? FP4Q_OK : FP4Q_ERR_ALIGNMENT;
+}
+
+fp4q_status device_status(hipError_t e) { return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_DEVICE; }
+
+int unit_of(int x_dt, int block, int H) {
+    int u = 16 / elem_size(x_dt);
+    if (block > u) u = block;
+    if (H > u) u = H;
+    return u;
+}
+
+#define FP4Q_TRY(expr)                           \
+    do {                                         \
+        fp4q_status st_ = (expr);                \
+        if (st_ != FP4Q_OK) return st_;          \
+    } while (0)
+
+// Shared body of fp4q_quantize and fp4q_scale_search.
+fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,
+                      int64_t ld_x, uint8_t* codes, uint8_t* scales, float* g_dev, void* dequant,
+                      int dq_dt, int64_t ld_dq, float* mse, float* sse, void* workspace,
+                      void* stream) {
+    const int B = cfg->block, H = cfg->hadamard;
+    FP4Q_TRY(check_dims(rows, cols, B, H));
+    const bool need_g = cfg->global_mode != FP4Q_GLOBAL_NONE;
+    if (need_g && !g_dev) return FP4Q_ERR_INVALID_ARG;
+    if (g_dev && ((uintptr_t)g_dev & 3u)) return FP4Q_ERR_ALIGNMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (rows == 0 || cols == 0) {
+        // nothing is read or written except g (1 for an empty tensor, or the user's)
+        if (!dtype_ok(x_dt) || (dequant && !dtype_ok(dq_dt))) return FP4Q_ERR_INVALID_ARG;
+        const float g_fixed = cfg->global_mode == FP4Q_GLOBAL_USER ? cfg->global_scale : 1.0f;
+        if (g_dev) return device_status(launch_write_g(g_dev, g_fixed, s));
+        return FP4Q_OK;
+    }
+    FP4Q_TRY(check_tensor(x, x_dt, rows, cols, ld_x));
+    FP4Q_TRY(check_buffer(scales));
+    if (codes) FP4Q_TRY(check_buffer(codes));
+    if (dequant) FP4Q_TRY(check_tensor(dequant, dq_dt, rows, cols, ld_dq));
+    if (mse) FP4Q_TRY(check_buffer(mse));
+    if (sse) FP4Q_TRY(check_buffer(sse));
+    const bool tamax = cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX;
+    if (tamax) FP4Q_TRY(check_buffer(workspace));
+
+    if (tamax) {
+        const int U = unit_of(x_dt, 1, H);
+        AmaxArgs aa{};
+        aa.x = x;
+        aa.ld_x = ld_x;
+        aa.units = rows * cols / U;
+        aa.units_per_row = cols / U;
+        aa.contiguous = ld_x == cols;
+        aa.partials = reinterpret_cast<uint32_t*>(workspace);
+        FP4Q_TRY(device_status(launch_amax(aa, x_dt, H, kAmaxBlocks, s)));
+    }
+
+    const int U = unit_of(x_dt, B, H);
+    QuantArgs qa{};
+    qa.x = x;
+    qa.ld_x = ld_x;
+    qa.cols = cols;
+    qa.units = rows * cols / U;
+    qa.units_per_row = cols / U;
+    qa.contiguous = ld_x == cols && (!dequant || ld_dq == cols);
+    qa.codes = codes;
+    qa.scales = scales;
+    qa.g_out = g_dev;
+    qa.dq = dequant;
+    qa.ld_dq = ld_dq;
+    qa.dq_dt = dq_dt;
+    qa.mse = mse;
+    qa.sse = sse;
+    qa.amax_partials = reinterpret_cast<const uint32_t*>(workspace);
+    qa.n_partials = tamax ? kAmaxBlocks : 0;
+    qa.global_mode = cfg->global_mode;
+    qa.user_g = cfg->global_scale;
+    qa.prevent_zero = cfg->strategy == FP4Q_PREVENT_ZERO;
+    const int grid = grid_for(qa.units);
+    hipError_t e;
+    switch (x_dt) {
+    case FP4Q_F32: e = launch_quant_f32(qa, B, H, cfg->scale_fmt, cfg->strategy, grid, s); break;
+    case FP4Q_BF16: e = launch_quant_bf16(qa, B, H, cfg->scale_fmt, cfg->strategy, grid, s); break;
+    default: e = launch_quant_f16(qa, B, H, cfg->scale_fmt, cfg->strategy, grid, s); break;
+    }
+    return device_status(e);
+}
+
+// g_dev of the calls that read a scale: must be NULL for E8M0.
+fp4q_status check_g_in(const fp4q_config* cfg, const float* g_dev) {
+    if (g_dev && cfg->scale_fmt == FP4Q_SCALE_E8M0) return FP4Q_ERR_UNSUPPORTED;
+    if (g_dev && ((uintptr_t)g_dev & 3u)) return FP4Q_ERR_ALIGNMENT;
+    return FP4Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
+
+const char* fp4q_status_string(int status) {
+    switch (status) {
+    case FP4Q_OK: return "ok";
+    case FP4Q_ERR_INVALID_ARG: return "invalid argument";
+    case FP4Q_ERR_UNSUPPORTED: return "unsupported combination";
+    case FP4Q_ERR_SHAPE: return "shape does not tile into blocks";
+    case FP4Q_ERR_ALIGNMENT: return "pointer or row pitch not 16-byte aligned";
+    case FP4Q_ERR_DEVICE: return "device launch failed";
+    }
+    return "unknown status";
+}
+
+size_t fp4q_workspace_bytes(const fp4q_config* cfg, int64_t rows, int64_t cols) {
+    (void)rows;
+    (void)cols;
+    if (!cfg) return 0;
+    return cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX ? (size_t)kAmaxBlocks * sizeof(uint32_t) : 0;
+}
+
+fp4q_status fp4q_quantize(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,
+                          int64_t ld_x, uint8_t* codes, uint8_t* scales, float* g_dev, void* dequant,
+                          int dq_dt, int64_t ld_dq, float* block_mse, void* workspace, void* stream) {
+    FP4Q_TRY(check_config(cfg));
+    if (!codes && rows > 0 && cols > 0) return FP4Q_ERR_INVALID_ARG;
+    return run_quant(cfg, x, x_dt, rows, cols, ld_x, codes, scales, g_dev, dequant, dq_dt, ld_dq,
+                     block_mse, nullptr, workspace, stream);
+}
+
+fp4q_status fp4q_scale_search(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows,
+                              int64_t cols, int64_t ld_x, uint8_t* scales, float* g_dev,
+                              float* best_sse, void* workspace, void* stream) {
+    FP4Q_TRY(check_config(cfg));
+    if (cfg->strategy == FP4Q_GIVEN) return FP4Q_ERR_INVALID_ARG;
+    return run_quant(cfg, x, x_dt, rows, cols, ld_x, nullptr, scales, g_dev, nullptr, FP4Q_F32, cols,
+                     nullptr, best_sse, workspace, stream);
+}
+
+fp4q_status fp4q_dequantize(const fp4q_config* cfg, const uint8_t* codes, const uint8_t* scales,
+                            const float* g_dev, int64_t rows, int64_t cols, void* out, int out_dt,
+                            int64_t ld_out, void* stream) {
+    FP4Q_TRY(check_config(cfg));
+    const int B = cfg->block;
+    FP4Q_TRY(check_dims(rows, cols, B, 0));
+    FP4Q_TRY(check_g_in(cfg, g_dev));
+    if (rows == 0 || cols == 0) return dtype_ok(out_dt) ? FP4Q_OK : FP4Q_ERR_INVALID_ARG;
+    FP4Q_TRY(check_buffer(codes));
+    FP4Q_TRY(check_buffer(scales));
+    FP4Q_TRY(check_tensor(out, out_dt, rows, cols, ld_out));
+    const int U = B > 4 ? B : 4;
+    DequantArgs a{};
+    a.codes = codes;
+    a.scales = scales;
+    a.g_dev = g_dev;
+    a.scale_fmt = cfg->scale_fmt;
+    a.cols = cols;
+    a.units = rows * cols / U;
+    a.units_per_row = cols / U;
+    a.out = out;
+    a.ld_out = ld_out;
+    a.out_dt = out_dt;
+    return device_status(launch_dequant(a, B, grid_for(a.units), (hipStream_t)stream));
+}
+
+fp4q_status fp4q_block_mse(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,
+                           int64_t ld_x, const uint8_t* codes, const uint8_t* scales,
+                           const float* g_dev, float* block_mse, void* stream) {
+    FP4Q_TRY(check_config(cfg));
+    const int B = cfg->block, H = cfg->hadamard;
+    FP4Q_TRY(check_dims(rows, cols, B, H));
+    FP4Q_TRY(check_g_in(cfg, g_dev));
+    if (rows == 0 || cols == 0) return dtype_ok(x_dt) ? FP4Q_OK : FP4Q_ERR_INVALID_ARG;
+    FP4Q_TRY(check_tensor(x, x_dt, rows, cols, ld_x));
+    FP4Q_TRY(check_buffer(codes));
+    FP4Q_TRY(check_buffer(scales));
+    FP4Q_TRY(check_buffer(block_mse));
+    const int U = unit_of(x_dt, B, H);
+    MseArgs a{};
+    a.x = x;
+    a.ld_x = ld_x;
+    a.cols = cols;
+    a.units = rows * cols / U;
+    a.units_per_row = cols / U;
+    a.codes = codes;
+    a.scales = scales;
+    a.g_dev = g_dev;
+    a.scale_fmt = cfg->scale_fmt;
+    a.mse = block_mse;
+    return device_status(launch_block_mse(a, x_dt, B, H, grid_for(a.units), (hipStream_t)stream));
+}
+
+static fp4q_status check_relaxed(const fp4q_config* cfg, const void* w, int w_dt, int64_t rows,
+                                 int64_t cols, int64_t ld_w, const uint8_t* scales, const float* g_dev,
+                                 const uint16_t* c_f16, int32_t sub_block) {
+    FP4Q_TRY(check_config(cfg));
+    if (cfg->hadamard != 0) return FP4Q_ERR_UNSUPPORTED;
+    const int B = cfg->block;
+    if (sub_block != 4 && sub_block != 8 && sub_block != 16 && sub_block != 32) return FP4Q_ERR_SHAPE;
+    if (B % sub_block != 0) return FP4Q_ERR_SHAPE;
+    FP4Q_TRY(check_dims(rows, cols, B, 0));
+    FP4Q_TRY(check_g_in(cfg, g_dev));
+    if (rows == 0 || cols == 0) return dtype_ok(w_dt) ? FP4Q_OK : FP4Q_ERR_INVALID_ARG;
+    FP4Q_TRY(check_tensor(w, w_dt, rows, cols, ld_w));
+    FP4Q_TRY(check_buffer(scales));
+    FP4Q_TRY(check_buffer(c_f16));
+    return FP4Q_OK;
+}
+
+fp4q_status fp4q_relaxed_fakequant_fwd(const fp4q_config* cfg, const void* w, int w_dt, int64_t rows,
+                                       int64_t cols, int64_t ld_w, const uint8_t* scales,
+                                       const float* g_dev, const uint16_t* c_f16, int32_t sub_block,
+                                       void* w_hat, int out_dt, int64_t ld_out, uint8_t* codes,
+                                       void* stream) {
+    FP4Q_TRY(check_relaxed(cfg, w, w_dt, rows, cols, ld_w, scales, g_dev, c_f16, sub_block));
+    if (rows == 0 || cols == 0) return dtype_ok(out_dt) ? FP4Q_OK : FP4Q_ERR_INVALID_ARG;
+    FP4Q_TRY(check_tensor(w_hat, out_dt, rows, cols, ld_out));
+    if (codes) FP4Q_TRY(check_buffer(codes));
+    const int U = unit_of(w_dt, cfg->block, 0);
+    RelaxedArgs a{};
+    a.w = w;
+    a.ld_w = ld_w;
+    a.cols = cols;
+    a.units = rows * cols / U;
+    a.units_per_row = cols / U;
+    a.scales = scales;
+    a.g_dev = g_dev;
+    a.scale_fmt = cfg->scale_fmt;
+    a.c = c_f16;
+    a.w_hat = w_hat;
+    a.ld_out = ld_out;
+    a.out_dt = out_dt;
+    a.codes = codes;
+    return device_status(
+        launch_relaxed_fwd(a, w_dt, cfg->block, sub_block, grid_for(a.units), (hipStream_t)stream));
+}
+
+fp4q_status fp4q_relaxed_fakequant_bwd(const fp4q_config* cfg, const void* w, int w_dt, int64_t rows,
+                                       int64_t cols, int64_t ld_w, const uint8_t* scales,
+                                       const float* g_dev, const uint16_t* c_f16, int32_t sub_block,
+                                       const void* grad_out, int g_dt, int64_t ld_g, float* grad_c,
+                                       void* stream) {
+    FP4Q_TRY(check_relaxed(cfg, w, w_dt, rows, cols, ld_w, scales, g_dev, c_f16, sub_block));
+    if (rows == 0 || cols == 0) return dtype_ok(g_dt) ? FP4Q_OK : FP4Q_ERR_INVALID_ARG;
+    FP4Q_TRY(check_tensor(grad_out, g_dt, rows, cols, ld_g));
+    FP4Q_TRY(check_buffer(grad_c));
+    const int U = unit_of(w_dt, cfg->block, 0);
+    RelaxedArgs a{};
+    a.w = w;
+    a.ld_w = ld_w;
+    a.cols = cols;
+    a.units = rows * cols / U;
+    a.units_per_row = cols / U;
+    a.scales = scales;
+    a.g_dev = g_dev;
+    a.scale_fmt = cfg->scale_fmt;
+    a.c = c_f16;
+    a.grad = grad_out;
+    a.ld_g = ld_g;
+    a.g_dt = g_dt;
+    a.grad_c = grad_c;
+    return device_status(
+        launch_relaxed_bwd(a, w_dt, cfg->block, sub_block, grid_for(a.units), (hipStream_t)stream));
+}
+
+}  // extern "C"

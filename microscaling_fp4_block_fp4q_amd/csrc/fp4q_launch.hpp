@@ -1,0 +1,74 @@
+// fp4q_launch.hpp -- host-side launch entry points of the kernel
+// translation units (internal to libfp4q.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fp4q_kernels.hpp"
+
+namespace fp4q_dev {
+
+// Quantize launch for one input dtype (fp32 / bf16 / fp16 translation units).
+hipError_t launch_quant_f32(const QuantArgs& a, int B, int H, int sf, int st, int grid, hipStream_t s);
+hipError_t launch_quant_bf16(const QuantArgs& a, int B, int H, int sf, int st, int grid, hipStream_t s);
+hipError_t launch_quant_f16(const QuantArgs& a, int B, int H, int sf, int st, int grid, hipStream_t s);
+
+hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t s);
+hipError_t launch_write_g(float* g_dev, float g, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, int B, int grid, hipStream_t s);
+hipError_t launch_block_mse(const MseArgs& a, int x_dt, int B, int H, int grid, hipStream_t s);
+hipError_t launch_relaxed_fwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s);
+hipError_t launch_relaxed_bwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s);
+
+// Template dispatch over block size, rotation size, scale format and strategy.
+template <class InT, int B, int H, int SF, int ST>
+hipError_t launch_quant_t(const QuantArgs& a, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((k_quant<InT, B, H, SF, ST>), dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class InT, int B, int H, int SF>
+hipError_t dispatch_quant_st(const QuantArgs& a, int st, int grid, hipStream_t s) {
+    switch (st) {
+    case ST_ABSMAX:
+    case ST_PREVENT_ZERO:
+        return launch_quant_t<InT, B, H, SF, ST_ABSMAX>(a, grid, s);
+    case ST_FOUR_OVER_SIX:
+        if constexpr (SF == SF_E4M3) return launch_quant_t<InT, B, H, SF, ST_FOUR_OVER_SIX>(a, grid, s);
+        return hipErrorInvalidValue;
+    case ST_BRUTE_FORCE:
+        return launch_quant_t<InT, B, H, SF, ST_BRUTE_FORCE>(a, grid, s);
+    case ST_GIVEN:
+        return launch_quant_t<InT, B, H, SF, ST_GIVEN>(a, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class InT, int B, int H>
+hipError_t dispatch_quant_sf(const QuantArgs& a, int sf, int st, int grid, hipStream_t s) {
+    return sf == SF_E8M0 ? dispatch_quant_st<InT, B, H, SF_E8M0>(a, st, grid, s)
+                         : dispatch_quant_st<InT, B, H, SF_E4M3>(a, st, grid, s);
+}
+
+template <class InT, int B>
+hipError_t dispatch_quant_h(const QuantArgs& a, int H, int sf, int st, int grid, hipStream_t s) {
+    switch (H) {
+    case 0: return dispatch_quant_sf<InT, B, 0>(a, sf, st, grid, s);
+    case 16: return dispatch_quant_sf<InT, B, 16>(a, sf, st, grid, s);
+    case 32: return dispatch_quant_sf<InT, B, 32>(a, sf, st, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class InT>
+hipError_t dispatch_quant(const QuantArgs& a, int B, int H, int sf, int st, int grid, hipStream_t s) {
+    switch (B) {
+    case 4: return dispatch_quant_h<InT, 4>(a, H, sf, st, grid, s);
+    case 8: return dispatch_quant_h<InT, 8>(a, H, sf, st, grid, s);
+    case 16: return dispatch_quant_h<InT, 16>(a, H, sf, st, grid, s);
+    case 32: return dispatch_quant_h<InT, 32>(a, H, sf, st, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fp4q_dev

@@ -1,0 +1,11 @@
+// quant_f16.hip -- quantize kernels for f16 input (one translation unit per
+// input dtype so the instantiations compile in parallel).
+#include "fp4q_launch.hpp"
+
+namespace fp4q_dev {
+
+hipError_t launch_quant_f16(const QuantArgs& a, int B, int H, int sf, int st, int grid, hipStream_t s) {
+    return dispatch_quant<f16_t>(a, B, H, sf, st, grid, s);
+}
+
+}  // namespace fp4q_dev

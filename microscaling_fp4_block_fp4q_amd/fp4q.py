@@ -1,0 +1,268 @@
+"""Thin ctypes binding of libfp4q.so (include/fp4q.h).
+
+Argument marshalling only: torch tensors become device pointers, element
+types and row strides; the current torch stream becomes the hipStream_t.
+Every step of the quantize-dequantize path runs in the library's HIP
+kernels.  There is no CPU fallback: a missing library raises.
+
+The raw entry points keep the C names (``fp4q_quantize`` ...); the short
+names (``quantize`` ...) also allocate the outputs with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfp4q.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "fp4q.h")
+
+# enums (include/fp4q.h)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE = range(6)
+F32, BF16, F16 = 0, 1, 2
+E8M0, E4M3 = 0, 1
+ABSMAX, PREVENT_ZERO, FOUR_OVER_SIX, BRUTE_FORCE, GIVEN = range(5)
+GLOBAL_NONE, GLOBAL_TENSOR_AMAX, GLOBAL_USER = range(3)
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("scale_fmt", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("strategy", ctypes.c_int32),
+        ("global_mode", ctypes.c_int32),
+        ("global_scale", ctypes.c_float),
+        ("hadamard", ctypes.c_int32),
+    ]
+
+
+def config(scale_fmt=E4M3, block=16, strategy=ABSMAX, global_mode=GLOBAL_NONE, global_scale=1.0,
+           hadamard=0) -> Config:
+    return Config(ctypes.sizeof(Config), scale_fmt, block, strategy, global_mode, global_scale, hadamard)
+
+
+def mxfp4(strategy=ABSMAX, hadamard=0) -> Config:
+    """E2M1 in blocks of 32 with a power-of-two E8M0 scale."""
+    return config(E8M0, 32, strategy, GLOBAL_NONE, 1.0, hadamard)
+
+
+def nvfp4(strategy=ABSMAX, global_mode=GLOBAL_TENSOR_AMAX, global_scale=1.0, hadamard=0) -> Config:
+    """E2M1 in blocks of 16 with an E4M3 scale under a per-tensor fp32 scale."""
+    return config(E4M3, 16, strategy, global_mode, global_scale, hadamard)
+
+
+class Fp4qError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfp4q.so (built by microscaling_fp4_block_fp4q_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m microscaling_fp4_block_fp4q_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, p, cp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(Config)
+        L.fp4q_abi_version.restype = ctypes.c_int
+        L.fp4q_abi_version.argtypes = []
+        L.fp4q_status_string.restype = ctypes.c_char_p
+        L.fp4q_status_string.argtypes = [ctypes.c_int]
+        L.fp4q_workspace_bytes.restype = ctypes.c_size_t
+        L.fp4q_workspace_bytes.argtypes = [cp, i64, i64]
+        L.fp4q_quantize.restype = ctypes.c_int
+        L.fp4q_quantize.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, p, ctypes.c_int, i64, p, p, p]
+        L.fp4q_dequantize.restype = ctypes.c_int
+        L.fp4q_dequantize.argtypes = [cp, p, p, p, i64, i64, p, ctypes.c_int, i64, p]
+        L.fp4q_block_mse.restype = ctypes.c_int
+        L.fp4q_block_mse.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, p, p]
+        L.fp4q_scale_search.restype = ctypes.c_int
+        L.fp4q_scale_search.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, p, p]
+        L.fp4q_relaxed_fakequant_fwd.restype = ctypes.c_int
+        L.fp4q_relaxed_fakequant_fwd.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, i32, p,
+                                                 ctypes.c_int, i64, p, p]
+        L.fp4q_relaxed_fakequant_bwd.restype = ctypes.c_int
+        L.fp4q_relaxed_fakequant_bwd.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, i32, p,
+                                                 ctypes.c_int, i64, p, p]
+        _lib = L
+    return _lib
+
+
+def declared_entry_points() -> list[str]:
+    """Function names include/fp4q.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(fp4q_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().fp4q_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return lib().fp4q_abi_version()
+
+
+def workspace_bytes(cfg: Config, rows: int, cols: int) -> int:
+    return lib().fp4q_workspace_bytes(ctypes.byref(cfg), rows, cols)
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported element type {t.dtype}") from None
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _rows_cols_ld(t: torch.Tensor):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise Fp4qError(status, what)
+
+
+# --------------------------------------------------------------------------
+# raw entry points (caller allocates every buffer)
+# --------------------------------------------------------------------------
+
+def fp4q_quantize(cfg, x, codes, scales, g=None, dequant=None, block_mse=None, workspace=None, stream=None):
+    rows, cols, ld = _rows_cols_ld(x)
+    dq_dt, ld_dq = F32, cols
+    if dequant is not None:
+        _, _, ld_dq = _rows_cols_ld(dequant)
+        dq_dt = dtype_code(dequant)
+    st = lib().fp4q_quantize(ctypes.byref(cfg), _ptr(x), dtype_code(x), rows, cols, ld, _ptr(codes),
+                             _ptr(scales), _ptr(g), _ptr(dequant), dq_dt, ld_dq, _ptr(block_mse),
+                             _ptr(workspace), _stream(stream))
+    _check(st, "fp4q_quantize")
+
+
+def fp4q_scale_search(cfg, x, scales, g=None, best_sse=None, workspace=None, stream=None):
+    rows, cols, ld = _rows_cols_ld(x)
+    st = lib().fp4q_scale_search(ctypes.byref(cfg), _ptr(x), dtype_code(x), rows, cols, ld, _ptr(scales),
+                                 _ptr(g), _ptr(best_sse), _ptr(workspace), _stream(stream))
+    _check(st, "fp4q_scale_search")
+
+
+def fp4q_dequantize(cfg, codes, scales, out, g=None, stream=None):
+    rows, cols, ld = _rows_cols_ld(out)
+    st = lib().fp4q_dequantize(ctypes.byref(cfg), _ptr(codes), _ptr(scales), _ptr(g), rows, cols, _ptr(out),
+                               dtype_code(out), ld, _stream(stream))
+    _check(st, "fp4q_dequantize")
+
+
+def fp4q_block_mse(cfg, x, codes, scales, block_mse, g=None, stream=None):
+    rows, cols, ld = _rows_cols_ld(x)
+    st = lib().fp4q_block_mse(ctypes.byref(cfg), _ptr(x), dtype_code(x), rows, cols, ld, _ptr(codes),
+                              _ptr(scales), _ptr(g), _ptr(block_mse), _stream(stream))
+    _check(st, "fp4q_block_mse")
+
+
+def fp4q_relaxed_fakequant_fwd(cfg, w, scales, c, sub_block, w_hat, g=None, codes=None, stream=None):
+    rows, cols, ld = _rows_cols_ld(w)
+    _, _, ld_out = _rows_cols_ld(w_hat)
+    st = lib().fp4q_relaxed_fakequant_fwd(ctypes.byref(cfg), _ptr(w), dtype_code(w), rows, cols, ld,
+                                          _ptr(scales), _ptr(g), _ptr(c), sub_block, _ptr(w_hat),
+                                          dtype_code(w_hat), ld_out, _ptr(codes), _stream(stream))
+    _check(st, "fp4q_relaxed_fakequant_fwd")
+
+
+def fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g=None, stream=None):
+    rows, cols, ld = _rows_cols_ld(w)
+    _, _, ld_g = _rows_cols_ld(grad_out)
+    st = lib().fp4q_relaxed_fakequant_bwd(ctypes.byref(cfg), _ptr(w), dtype_code(w), rows, cols, ld,
+                                          _ptr(scales), _ptr(g), _ptr(c), sub_block, _ptr(grad_out),
+                                          dtype_code(grad_out), ld_g, _ptr(grad_c), _stream(stream))
+    _check(st, "fp4q_relaxed_fakequant_bwd")
+
+
+# --------------------------------------------------------------------------
+# allocating wrappers
+# --------------------------------------------------------------------------
+
+def _workspace(cfg, rows, cols, device):
+    n = workspace_bytes(cfg, rows, cols)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
+
+
+def quantize(x, cfg, dequant_dtype=None, want_mse=True, scales=None, stream=None):
+    """Quantize a 2-D device tensor; returns dict(codes, scales, g, dequant, mse)."""
+    rows, cols, _ = _rows_cols_ld(x)
+    dev = x.device
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // cfg.block), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    dq = None if dequant_dtype is None else torch.empty((rows, cols), dtype=dequant_dtype, device=dev)
+    mse = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=dev) if want_mse else None
+    fp4q_quantize(cfg, x, codes, scales, g, dq, mse, _workspace(cfg, rows, cols, dev), stream)
+    return dict(codes=codes, scales=scales, g=g, dequant=dq, mse=mse)
+
+
+def scale_search(x, cfg, want_sse=True, stream=None):
+    rows, cols, _ = _rows_cols_ld(x)
+    dev = x.device
+    scales = torch.empty((rows, cols // cfg.block), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    sse = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=dev) if want_sse else None
+    fp4q_scale_search(cfg, x, scales, g, sse, _workspace(cfg, rows, cols, dev), stream)
+    return dict(scales=scales, g=g, sse=sse)
+
+
+def dequantize(codes, scales, cfg, g=None, out_dtype=torch.float32, stream=None):
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    fp4q_dequantize(cfg, codes, scales, out, g, stream)
+    return out
+
+
+def block_mse(x, codes, scales, cfg, g=None, stream=None):
+    rows, cols, _ = _rows_cols_ld(x)
+    out = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=x.device)
+    fp4q_block_mse(cfg, x, codes, scales, out, g, stream)
+    return out
+
+
+def relaxed_fakequant_fwd(w, scales, c, cfg, sub_block=8, g=None, out_dtype=None, want_codes=False, stream=None):
+    rows, cols, _ = _rows_cols_ld(w)
+    w_hat = torch.empty((rows, cols), dtype=out_dtype or w.dtype, device=w.device)
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device) if want_codes else None
+    fp4q_relaxed_fakequant_fwd(cfg, w, scales, c, sub_block, w_hat, g, codes, stream)
+    return w_hat, codes
+
+
+def relaxed_fakequant_bwd(w, scales, c, grad_out, cfg, sub_block=8, g=None, stream=None):
+    rows, cols, _ = _rows_cols_ld(w)
+    grad_c = torch.empty((rows, cols // sub_block), dtype=torch.float32, device=w.device)
+    fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g, stream)
+    return grad_c

@@ -389,6 +389,18 @@ float oracle_global_scale(const float* y, int64_t n)
     return (g == 0.0f) ? 1.0f : g;
 }
 
+/* Per-tensor scale of a whole [rows, cols] tensor (rotated first when
+ * H != 0), as the hierarchical mode computes it; lets a test quantize a
+ * sample of rows with the scale of the full tensor. */
+float oracle_tensor_global_scale(const void* x, int x_dt, int64_t rows, int64_t cols, int64_t ld_x, int H)
+{
+    float* y = widen_and_rotate(x, x_dt, rows, cols, ld_x, H);
+    if (!y) return canonical_nan(0);
+    float g = oracle_global_scale(y, rows * cols);
+    free(y);
+    return g;
+}
+
 /* Quantize a [rows, cols] tensor in blocks of B along each row.
  * Outputs (each may be NULL): packed codes [rows, cols/2] (low nibble = even
  * column), scales [rows, cols/B] (input when strategy is GIVEN), g_out,

@@ -60,6 +60,8 @@ def lib():
         L.oracle_tree_sum.argtypes, L.oracle_tree_sum.restype = [p, i], f
         L.oracle_block_sse.argtypes, L.oracle_block_sse.restype = [p, i, f], f
         L.oracle_global_scale.argtypes, L.oracle_global_scale.restype = [p, i64], f
+        L.oracle_tensor_global_scale.argtypes = [p, i, i64, i64, i64, i]
+        L.oracle_tensor_global_scale.restype = f
         L.oracle_quantize.argtypes = [i, i, i, i, f, i, p, i, i64, i64, i64,
                                       p, p, p, p, i, i64, p, p]
         L.oracle_quantize.restype = i
@@ -161,6 +163,14 @@ def block_sse(y: np.ndarray, S: float) -> np.float32:
 def global_scale(y: np.ndarray) -> np.float32:
     a = np.ascontiguousarray(y, dtype=np.float32)
     return np.float32(lib().oracle_global_scale(_ptr(a), a.size))
+
+
+def tensor_global_scale(x: np.ndarray, *, hadamard: int = 0, x_dt: int | None = None) -> np.float32:
+    """g of hierarchical scaling for a whole tensor (rotated when hadamard != 0)."""
+    rows, cols = x.shape
+    xd = _dt_of(x, x_dt)
+    x = np.ascontiguousarray(x)
+    return np.float32(lib().oracle_tensor_global_scale(_ptr(x), xd, rows, cols, cols, hadamard))
 
 
 # --------------------------------------------------------------------------

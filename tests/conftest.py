@@ -19,3 +19,11 @@ def O():
     from oracle import oracle
     oracle.build()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def O_lib(O):
+    """Oracle plus the HIP library; a missing library is an error, not a skip."""
+    from microscaling_fp4_block_fp4q_amd import fp4q
+    fp4q.lib()
+    return O

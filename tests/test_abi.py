@@ -1,0 +1,124 @@
+"""The C ABI of libfp4q.so without a GPU: it loads, exports every function
+include/fp4q.h declares, and rejects bad arguments synchronously with the
+documented status codes before anything is launched.
+
+The pointers passed here are fake host addresses; every call below must be
+rejected by host-side validation, so no kernel ever sees them.  To keep it
+that way on a machine with a GPU, the validation cases only run where no
+GPU device node exists.
+"""
+import ctypes
+import os
+
+import pytest
+
+from microscaling_fp4_block_fp4q_amd import fp4q as F
+
+HAVE_LIB = os.path.exists(F.LIB_PATH)
+NO_GPU = not os.path.exists("/dev/kfd")
+needs_lib = pytest.mark.skipif(not HAVE_LIB, reason="libfp4q.so not built")
+cpu_only = pytest.mark.skipif(not NO_GPU, reason="fake-pointer validation runs only without a GPU")
+
+P = ctypes.c_void_p
+A = 0x10000          # a 16-byte-aligned fake address, never dereferenced
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    L = F.lib()
+    names = F.declared_entry_points()
+    assert set(names) >= {"fp4q_quantize", "fp4q_dequantize", "fp4q_block_mse", "fp4q_scale_search",
+                          "fp4q_relaxed_fakequant_fwd", "fp4q_relaxed_fakequant_bwd",
+                          "fp4q_abi_version", "fp4q_status_string", "fp4q_workspace_bytes"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@needs_lib
+def test_version_strings_workspace():
+    assert F.abi_version() == 1
+    for s in range(6):
+        assert F.status_string(s) and F.status_string(s) != "unknown status"
+    assert F.status_string(99) == "unknown status"
+    assert F.workspace_bytes(F.nvfp4(), 4096, 4096) >= 4
+    assert F.workspace_bytes(F.mxfp4(), 4096, 4096) == 0
+    assert F.lib().fp4q_workspace_bytes(None, 1, 1) == 0
+
+
+def quant(cfg, x=A, x_dt=F.F32, rows=16, cols=64, ld=64, codes=A, scales=A, g=A, dq=None, dq_dt=F.F32,
+          ld_dq=64, mse=None, ws=A):
+    return F.lib().fp4q_quantize(ctypes.byref(cfg) if cfg is not None else None, P(x), x_dt, rows, cols, ld,
+                                 P(codes), P(scales), P(g), P(dq), dq_dt, ld_dq, P(mse), P(ws), None)
+
+
+@needs_lib
+@cpu_only
+def test_quantize_validation():
+    nv = F.nvfp4()
+    assert quant(None) == F.ERR_INVALID_ARG
+    bad = F.nvfp4()
+    bad.struct_size = 4
+    assert quant(bad) == F.ERR_INVALID_ARG
+    assert quant(F.config(1, 12)) == F.ERR_SHAPE                       # block 12
+    assert quant(F.config(1, 16, 7)) == F.ERR_INVALID_ARG                        # strategy
+    assert quant(F.config(5, 16)) == F.ERR_INVALID_ARG                           # scale format
+    assert quant(F.config(1, 16, 0, 9)) == F.ERR_INVALID_ARG                     # global mode
+    assert quant(F.config(1, 16, hadamard=-16)) == F.ERR_INVALID_ARG
+    assert quant(F.config(1, 16, hadamard=64)) == F.ERR_UNSUPPORTED
+    assert quant(F.config(1, 16, hadamard=8)) == F.ERR_UNSUPPORTED
+    assert quant(F.config(0, 32, 0, F.GLOBAL_TENSOR_AMAX)) == F.ERR_UNSUPPORTED  # E8M0 + g
+    assert quant(F.config(0, 32, F.FOUR_OVER_SIX)) == F.ERR_UNSUPPORTED          # E8M0 + 4/6
+    for gs in (0.0, -1.0, float("inf"), float("nan"), 1e-39, 1e36):
+        assert quant(F.config(1, 16, 0, F.GLOBAL_USER, gs)) == F.ERR_INVALID_ARG, gs
+    assert quant(nv, x=0) == F.ERR_INVALID_ARG
+    assert quant(nv, codes=0) == F.ERR_INVALID_ARG
+    assert quant(nv, scales=0) == F.ERR_INVALID_ARG
+    assert quant(nv, g=0) == F.ERR_INVALID_ARG                                   # TENSOR_AMAX writes g
+    assert quant(nv, ws=0) == F.ERR_INVALID_ARG                                  # needs workspace
+    assert quant(nv, x_dt=7) == F.ERR_INVALID_ARG
+    assert quant(nv, rows=-1) == F.ERR_INVALID_ARG
+    assert quant(nv, cols=40, ld=40) == F.ERR_SHAPE                              # 40 % 16
+    assert quant(F.config(1, 16, hadamard=32), cols=48, ld=48) == F.ERR_SHAPE     # 48 % 32
+    assert quant(nv, ld=32) == F.ERR_SHAPE                                       # ld < cols
+    assert quant(nv, x=A + 4) == F.ERR_ALIGNMENT
+    assert quant(nv, codes=A + 8) == F.ERR_ALIGNMENT
+    assert quant(nv, ld=66) == F.ERR_ALIGNMENT                                   # 66 * 4 % 16
+    assert quant(F.config(1, 4), x_dt=F.BF16, cols=4, ld=8) == F.ERR_ALIGNMENT    # 4 bf16 = 8 bytes
+    assert quant(nv, dq=A, dq_dt=9) == F.ERR_INVALID_ARG
+    assert quant(nv, dq=A, ld_dq=8) == F.ERR_SHAPE
+    assert quant(nv, dq=A + 2) == F.ERR_ALIGNMENT
+    assert quant(nv, mse=A + 4) == F.ERR_ALIGNMENT
+
+
+@needs_lib
+@cpu_only
+def test_other_entry_points_validation():
+    L = F.lib()
+    nv, mx = F.nvfp4(), F.mxfp4()
+    r = ctypes.byref
+    # scale search rejects GIVEN
+    assert L.fp4q_scale_search(r(F.nvfp4(F.GIVEN)), P(A), 0, 16, 64, 64, P(A), P(A), None, P(A), None) == F.ERR_INVALID_ARG
+    # dequantize
+    assert L.fp4q_dequantize(r(nv), None, P(A), None, 16, 64, P(A), 0, 64, None) == F.ERR_INVALID_ARG
+    assert L.fp4q_dequantize(r(mx), P(A), P(A), P(A), 16, 64, P(A), 0, 64, None) == F.ERR_UNSUPPORTED   # g with E8M0
+    assert L.fp4q_dequantize(r(nv), P(A), P(A), None, 16, 72, P(A), 0, 72, None) == F.ERR_SHAPE
+    assert L.fp4q_dequantize(r(nv), P(A), P(A), None, 16, 64, P(A + 4), 0, 64, None) == F.ERR_ALIGNMENT
+    # block mse
+    assert L.fp4q_block_mse(r(nv), P(A), 0, 16, 64, 64, P(A), P(A), None, None, None) == F.ERR_INVALID_ARG
+    # relaxed fwd / bwd
+    fwd, bwd = L.fp4q_relaxed_fakequant_fwd, L.fp4q_relaxed_fakequant_bwd
+    assert fwd(r(F.mxfp4(hadamard=32)), P(A), 0, 16, 64, 64, P(A), None, P(A), 8, P(A), 0, 64, None, None) == F.ERR_UNSUPPORTED
+    assert fwd(r(mx), P(A), 0, 16, 64, 64, P(A), None, P(A), 6, P(A), 0, 64, None, None) == F.ERR_SHAPE
+    assert fwd(r(nv), P(A), 0, 16, 64, 64, P(A), None, P(A), 32, P(A), 0, 64, None, None) == F.ERR_SHAPE  # 16 % 32
+    assert fwd(r(mx), P(A), 0, 16, 64, 64, P(A), None, None, 8, P(A), 0, 64, None, None) == F.ERR_INVALID_ARG
+    assert fwd(r(mx), P(A), 0, 16, 64, 64, P(A), None, P(A), 8, None, 0, 64, None, None) == F.ERR_INVALID_ARG
+    assert bwd(r(mx), P(A), 0, 16, 64, 64, P(A), None, P(A), 8, P(A), 0, 64, None, None) == F.ERR_INVALID_ARG
+    assert bwd(r(mx), P(A), 0, 16, 64, 64, P(A), None, P(A), 8, None, 0, 64, P(A), None) == F.ERR_INVALID_ARG
+
+
+def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
+    """The product path has no fallback: a missing library is an error."""
+    monkeypatch.setattr(F, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(F, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        F.lib()
