@@ -213,19 +213,19 @@ fp4q_status fp4q_dequantize(const fp4q_config* cfg, const uint8_t* codes, const 
     FP4Q_TRY(check_buffer(codes));
     FP4Q_TRY(check_buffer(scales));
     FP4Q_TRY(check_tensor(out, out_dt, rows, cols, ld_out));
-    const int U = B > 4 ? B : 4;
+    const int DU = cols % 8 == 0 ? 8 : 4;     // output values per lane
     DequantArgs a{};
     a.codes = codes;
     a.scales = scales;
     a.g_dev = g_dev;
     a.scale_fmt = cfg->scale_fmt;
     a.cols = cols;
-    a.units = rows * cols / U;
-    a.units_per_row = cols / U;
+    a.units = rows * cols / DU;
+    a.units_per_row = cols / DU;
     a.out = out;
     a.ld_out = ld_out;
     a.out_dt = out_dt;
-    return device_status(launch_dequant(a, B, grid_for(a.units), (hipStream_t)stream));
+    return device_status(launch_dequant(a, B, DU, grid_for(a.units), (hipStream_t)stream));
 }
 
 fp4q_status fp4q_block_mse(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,

@@ -176,21 +176,40 @@ __device__ __forceinline__ int64_t unit_offset(int64_t u, int64_t upr, int64_t l
 // Encoding of one block at one scale
 // ---------------------------------------------------------------------------
 
-// Quantize y[OFF, OFF+B) at scale S (usable; invS = 1/S exactly for E8M0):
-// r[i] receives the E2M1 grid value of |y_i| / S; returns the block SSE.
-// For a power-of-two E8M0 scale, |y| * 2^-k is exactly the IEEE quotient
-// fl(|y| / 2^k); E4M3 scales use the correctly rounded division.
+// Scales for which the division-free quotient below is exact (see
+// quotient()): R = fl(1/S) is then a normal number and so is every residual.
+__device__ __forceinline__ bool fast_quotient_range(float S) { return S >= 0x1p-100f && S <= 0x1p100f; }
+
+// fl(a / S) for a >= 0.  E8M0: S is a power of two and R = 1/S exactly, so
+// the product is the correctly rounded quotient.  E4M3 with FAST: R =
+// fl(1/S); q0 = fl(a R) is within two ulps, the FMA residual a - q0 S is
+// exact, and one FMA correction gives the correctly rounded quotient (the
+// classic reciprocal-refinement argument; checked exhaustively for every
+// fp32 scale mantissa at every E2M1 bin boundary and at 6, the clip bound).
+// Otherwise the IEEE division (0 for S == 0).
+template <int SF, bool FAST>
+__device__ __forceinline__ float quotient(float a, float S, float R) {
+    if constexpr (SF == SF_E8M0) {
+        return a * R;
+    } else if constexpr (FAST) {
+        const float q0 = a * R;
+        const float rr = __builtin_fmaf(-q0, S, a);
+        return __builtin_fmaf(rr, R, q0);
+    } else {
+        return (S > 0.0f) ? a / S : 0.0f;
+    }
+}
+
+// Quantize y[OFF, OFF+B) at scale S (usable; R as for quotient()): r[i]
+// receives the E2M1 grid value of |y_i| / S; returns the block SSE.
 // NAN_GUARD: elements may be NaN (caller-given scales), which encode as 0.
-template <int SF, int B, int OFF, bool NAN_GUARD, int U>
-__device__ __forceinline__ float encode_block(const float (&y)[U], float S, float invS, float (&r)[B]) {
+template <int SF, int B, int OFF, bool NAN_GUARD, bool FAST, int U>
+__device__ __forceinline__ float encode_block(const float (&y)[U], float S, float R, float (&r)[B]) {
     float e[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) {
         const float a = fabsf(y[OFF + i]);
-        float u;
-        if constexpr (SF == SF_E8M0) u = a * invS;
-        else u = (S > 0.0f) ? a / S : 0.0f;
-        float rr = e2m1_round(u);
+        float rr = e2m1_round(quotient<SF, FAST>(a, S, R));
         if constexpr (NAN_GUARD) rr = (a == a) ? rr : 0.0f;
         r[i] = rr;
         const float d = a - rr * S;       // |y| - fl(grid * S): same magnitude as y - yhat
@@ -199,15 +218,148 @@ __device__ __forceinline__ float encode_block(const float (&y)[U], float S, floa
     return tree_sum<B>(e);
 }
 
+// encode_block at an E4M3 scale chosen per lane: division-free when S is in
+// range, IEEE division otherwise (zero scales, extreme g).
+template <int B, int OFF, bool NAN_GUARD, int U>
+__device__ __forceinline__ float encode_block_e4m3(const float (&y)[U], float S, float (&r)[B]) {
+    if (fast_quotient_range(S)) return encode_block<SF_E4M3, B, OFF, NAN_GUARD, true>(y, S, 1.0f / S, r);
+    return encode_block<SF_E4M3, B, OFF, NAN_GUARD, false>(y, S, 0.0f, r);
+}
+
+// Candidate scales of the brute-force search, one table per workgroup.
+// Entry c holds, for the scale S_c of code c (E4M3: fl(dec(c) g), c = 1..126;
+// E8M0: 2^(c-127), c = 0..254):
+//   x = S_c,  y = R_c (fl(1/S_c) when the division-free quotient applies,
+//   exact 2^(127-c) for E8M0),  z = T0_c, the largest fp32 a with
+//   fl(a / S_c) <= 0.25 (a that encodes to zero),  w = fl(6 S_c), the value a
+//   saturated element dequantizes to.
+struct BfTable {
+    float4 e[256];
+    bool fast;   // every candidate in the division-free range
+};
+
+// Largest fp32 a with a / S <= 0.25 + 2^-26 (the rounding boundary above
+// 0.25, which itself rounds down to 0.25): the product is exact in double
+// and is rounded toward zero to fp32.
+__device__ __forceinline__ float zero_bin_limit(float S) {
+    const double p = (0.25 + 0x1p-26) * (double)S;
+    float t = (float)p;
+    if ((double)t > p) t = as_f(as_u(t) - 1u);
+    return t;
+}
+
+template <int SF>
+__device__ __forceinline__ void fill_bf_table(BfTable& t, float g) {
+    constexpr uint32_t N = SF == SF_E8M0 ? 255u : 127u;
+    for (uint32_t c = threadIdx.x; c < N; c += kThreads) {
+        float S, R;
+        if constexpr (SF == SF_E8M0) {
+            S = e8m0_value(c);
+            R = e8m0_inverse(c);
+        } else {
+            S = e4m3_value(c) * g;
+            R = fast_quotient_range(S) ? 1.0f / S : 0.0f;
+        }
+        t.e[c] = make_float4(S, R, zero_bin_limit(S), 6.0f * S);
+    }
+    if (threadIdx.x == 0)
+        t.fast = SF == SF_E8M0 || (fast_quotient_range(e4m3_value(1u) * g) && fast_quotient_range(e4m3_value(0x7Eu) * g));
+    __syncthreads();
+}
+
+// Exact brute-force search ("Finer is Better (with the Right Scaling)",
+// method part 2: the scale with the least block MSE among all representable
+// ones; ties to the smaller code) by branch and bound.  Every skipped code
+// provably has a larger fp32 tree SSE than the best one found, so the result
+// is the exhaustive argmin:
+//  * start from the abs-max scale and its map-to-4 neighbour;
+//  * upper side: an element with a <= T0_c encodes to 0 at scale c and adds
+//    exactly fl(a*a) to the tree, so the tree over {fl(a*a) if a <= T0_c
+//    else 0} is a lower bound of SSE_c (fp32 addition is monotone) that only
+//    grows with c; codes from the first one whose bound exceeds the best
+//    are skipped, and once every element encodes to 0 (a_max <= T0_c) all
+//    larger codes tie with c, so nothing above c can win;
+//  * lower side: while fl(6 S_c) <= a_max the block maximum saturates and
+//    contributes fl((a_max - fl(6 S_c))^2) <= SSE_c, which shrinks as c
+//    grows; codes below the first one whose term is <= best are skipped.
+// The bounds are found by binary search (the predicates are monotone in c).
+template <int SF, int B, int OFF, bool FAST, int U>
+__device__ __forceinline__ void brute_force_block(const float (&y)[U], float a_b, uint32_t c_first, uint32_t c_second,
+                                                  const BfTable& t, uint32_t& best_code, float& best_sse) {
+    constexpr uint32_t CLO = SF == SF_E8M0 ? 0u : 1u;           // candidate codes [CLO, CEND)
+    constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : 127u;
+    float sq[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) sq[i] = y[OFF + i] * y[OFF + i];
+
+    // initial best: the two abs-max style candidates
+    {
+        float rc[B];
+        const float4 e1 = t.e[c_first];
+        best_sse = encode_block<SF, B, OFF, false, FAST>(y, e1.x, e1.y, rc);
+        best_code = c_first;
+        if (c_second != c_first) {
+            const float4 e2 = t.e[c_second];
+            const float s2 = encode_block<SF, B, OFF, false, FAST>(y, e2.x, e2.y, rc);
+            if (s2 < best_sse || (s2 == best_sse && c_second < best_code)) { best_sse = s2; best_code = c_second; }
+        }
+    }
+    const float best0 = best_sse;
+
+    // c_hi: first code whose zero-bin bound exceeds best0, or whose every
+    // element encodes to zero (then it is evaluated, larger codes are not)
+    uint32_t lo = CLO, hi = CEND;
+#pragma unroll 1
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        const float T0 = t.e[mid].z;
+        float z[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) z[i] = fabsf(y[OFF + i]) <= T0 ? sq[i] : 0.0f;
+        const bool stop = tree_sum<B>(z) > best0 || a_b <= T0;
+        if (stop) hi = mid; else lo = mid + 1;
+    }
+    uint32_t c_hi = lo;                                  // first code that stops the scan
+    if (c_hi < CEND && a_b <= t.e[c_hi].z) ++c_hi;       // the all-zero code itself may still win a tie
+
+    // c_star: codes below it saturate the block maximum
+    lo = CLO; hi = CEND;
+#pragma unroll 1
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (t.e[mid].w > a_b) hi = mid; else lo = mid + 1;
+    }
+    const uint32_t c_star = lo;                          // first code with fl(6 S) > a_max
+    // c_lo: first code in [CLO, c_star) whose saturation term is <= best0
+    lo = CLO; hi = c_star;
+#pragma unroll 1
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        const float d = a_b - t.e[mid].w;
+        if (d * d <= best0) hi = mid; else lo = mid + 1;
+    }
+    const uint32_t c_lo = lo;
+
+#pragma unroll 1
+    for (uint32_t c = c_lo; c < c_hi; ++c) {
+        if (c == c_first || c == c_second) continue;
+        const float4 e = t.e[c];
+        float rc[B];
+        const float s = encode_block<SF, B, OFF, false, FAST>(y, e.x, e.y, rc);
+        if (s < best_sse || (s == best_sse && c < best_code)) { best_sse = s; best_code = c; }
+    }
+}
+
 // Scale selection + encoding of block number BI of a unit.
 template <int SF, int ST, int B, int BI, int U>
 __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float six_g, float four_g,
-                                            int prevent_zero, uint32_t given, uint32_t (&code)[U],
-                                            float (&dq)[U], uint32_t& scale_code, float& sse) {
+                                            int prevent_zero, uint32_t given, const BfTable* bft,
+                                            uint32_t (&code)[U], float (&dq)[U], uint32_t& scale_code,
+                                            float& sse) {
     constexpr int OFF = BI * B;
     uint32_t sc;
     bool nan_block;
-    float S = 0.0f, invS = 0.0f;
+    float S = 0.0f;
     float r[B];
 
     if constexpr (ST == ST_GIVEN) {
@@ -215,13 +367,13 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
             sc = given & 0xFFu;
             nan_block = sc == kE8M0NaN;
             S = e8m0_value(sc);
-            invS = e8m0_inverse(sc);
+            if (!nan_block) sse = encode_block<SF, B, OFF, true, true>(y, S, e8m0_inverse(sc), r);
         } else {
             sc = given & 0x7Fu;
             S = e4m3_value(sc) * g;
             nan_block = sc == kE4M3NaN || !scale_usable(S);
+            if (!nan_block) sse = encode_block_e4m3<B, OFF, true>(y, S, r);
         }
-        if (!nan_block) sse = encode_block<SF, B, OFF, true>(y, S, invS, r);
     } else {
         uint32_t ab = 0;
 #pragma unroll
@@ -231,33 +383,26 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
         if (!nan_block) {
             if constexpr (SF == SF_E8M0) {
                 if constexpr (ST == ST_BRUTE_FORCE) {
-                    float best = __builtin_inff();
-                    uint32_t bc = 0;
-#pragma unroll 1
-                    for (uint32_t c = 0; c <= 254u; ++c) {
-                        float rc[B];
-                        float s = encode_block<SF, B, OFF, false>(y, e8m0_value(c), e8m0_inverse(c), rc);
-                        if (s < best) { best = s; bc = c; }
-                    }
-                    sc = bc;
+                    const uint32_t c0 = e8m0_absmax_code(ab);
+                    float best;
+                    brute_force_block<SF, B, OFF, true>(y, a_b, c0, c0 < 254u ? c0 + 1u : c0, *bft, sc, best);
                 } else {
                     sc = e8m0_absmax_code(ab);
                 }
                 S = e8m0_value(sc);
-                invS = e8m0_inverse(sc);
-                sse = encode_block<SF, B, OFF, false>(y, S, invS, r);
+                sse = encode_block<SF, B, OFF, false, true>(y, S, e8m0_inverse(sc), r);
             } else {
                 const uint32_t s6 = e4m3_encode(a_b / six_g);
                 if constexpr (ST == ST_ABSMAX) {
                     sc = (prevent_zero && s6 == 0u) ? 1u : s6;
                     S = e4m3_value(sc) * g;
-                    sse = encode_block<SF, B, OFF, false>(y, S, 0.0f, r);
+                    sse = encode_block_e4m3<B, OFF, false>(y, S, r);
                 } else if constexpr (ST == ST_FOUR_OVER_SIX) {
                     const uint32_t s4 = e4m3_encode(a_b / four_g);
                     const float S6 = e4m3_value(s6) * g, S4 = e4m3_value(s4) * g;
                     float r4[B];
-                    const float e6 = encode_block<SF, B, OFF, false>(y, S6, 0.0f, r);
-                    const float e4 = encode_block<SF, B, OFF, false>(y, S4, 0.0f, r4);
+                    const float e6 = encode_block_e4m3<B, OFF, false>(y, S6, r);
+                    const float e4 = encode_block_e4m3<B, OFF, false>(y, S4, r4);
                     const bool take4 = e4 < e6;   // equal error keeps the smaller code s6
                     sc = take4 ? s4 : s6;
                     S = take4 ? S4 : S6;
@@ -265,17 +410,13 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
 #pragma unroll
                     for (int i = 0; i < B; ++i) r[i] = take4 ? r4[i] : r[i];
                 } else {   // brute force over the 126 positive finite E4M3 scales
-                    float best = __builtin_inff();
-                    uint32_t bc = 1;
-#pragma unroll 1
-                    for (uint32_t c = 1; c <= 0x7Eu; ++c) {
-                        float rc[B];
-                        float s = encode_block<SF, B, OFF, false>(y, e4m3_value(c) * g, 0.0f, rc);
-                        if (s < best) { best = s; bc = c; }
-                    }
-                    sc = bc;
+                    const uint32_t s4 = e4m3_encode(a_b / four_g);
+                    const uint32_t c6 = s6 > 0u ? s6 : 1u, c4 = s4 > 0u ? s4 : 1u;
+                    float best;
+                    if (bft->fast) brute_force_block<SF, B, OFF, true>(y, a_b, c6, c4, *bft, sc, best);
+                    else brute_force_block<SF, B, OFF, false>(y, a_b, c6, c4, *bft, sc, best);
                     S = e4m3_value(sc) * g;
-                    sse = encode_block<SF, B, OFF, false>(y, S, 0.0f, r);
+                    sse = encode_block_e4m3<B, OFF, false>(y, S, r);
                 }
             }
         } else {
@@ -298,6 +439,83 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
             dq[OFF + i] = with_sign_of(r[i] * S, y[OFF + i]);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Coalesced tile I/O through LDS.  A wave owns a tile of 64 consecutive
+// units of a contiguous tensor.  Global memory is touched 16 bytes per lane
+// with consecutive lanes on consecutive addresses; LDS re-distributes the
+// bytes so that each lane holds its own unit.  Units sit in LDS slots padded
+// by 16 bytes, which spreads the 16-byte reads of 16 consecutive lanes over
+// all banks.  Only the owning wave touches its LDS region, so a wave-level
+// compiler barrier orders the exchange.
+// ---------------------------------------------------------------------------
+
+constexpr int kTileUnits = 64;
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bytes of one unit's LDS slot: U values of at most 4 bytes plus padding.
+template <int U>
+constexpr int slot_bytes() { return U * 4 + 16; }
+
+// Load the tile's input (nvalid units of U elements of type T starting at
+// base) and return this lane's unit widened to fp32.
+template <class T, int U>
+__device__ __forceinline__ void tile_load(const T* __restrict__ base, int nvalid, char* lds, int lane,
+                                          float (&y)[U]) {
+    constexpr int ES = ElemSize<T>::value;
+    constexpr int C = U * ES / 16;                   // 16-byte chunks per unit
+    constexpr int SLOT = slot_bytes<U>();
+    const int nchunks = nvalid * C;
+    const uint4* src = reinterpret_cast<const uint4*>(base);
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        const int j = k * 64 + lane;
+        if (j < nchunks) {
+            const uint4 v = src[j];
+            *reinterpret_cast<uint4*>(lds + (j / C) * SLOT + (j % C) * 16) = v;
+        }
+    }
+    wave_sync_lds();
+    load_elems<T, U>(reinterpret_cast<const T*>(lds + lane * SLOT), y);
+    wave_sync_lds();
+}
+
+// Store the lanes' U values (as type dt) of a tile of nvalid units to
+// out_base, coalesced.
+template <int U, int EO>
+__device__ __forceinline__ void tile_store_t(void* __restrict__ out_base, int dt, int nvalid, char* lds, int lane,
+                                             const float (&v)[U]) {
+    constexpr int BYTES = U * EO;
+    if constexpr (BYTES >= 16) {
+        constexpr int C = BYTES / 16;
+        constexpr int SLOT = slot_bytes<U>();
+        store_elems_rt<U>(lds + lane * SLOT, dt, 0, v);
+        wave_sync_lds();
+        uint4* dst = reinterpret_cast<uint4*>(out_base);
+        const int nchunks = nvalid * C;
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            const int j = k * 64 + lane;
+            if (j < nchunks) dst[j] = *reinterpret_cast<const uint4*>(lds + (j / C) * SLOT + (j % C) * 16);
+        }
+    } else {
+        // 8-byte units (4 values of 2 bytes): already contiguous per lane
+        if (lane < nvalid) store_elems_rt<U>(out_base, dt, (int64_t)lane * U, v);
+    }
+    wave_sync_lds();
+}
+
+template <int U>
+__device__ __forceinline__ void tile_store(void* __restrict__ out_base, int dt, int nvalid, char* lds, int lane,
+                                           const float (&v)[U]) {
+    if (dt == DT_F32) tile_store_t<U, 4>(out_base, dt, nvalid, lds, lane, v);
+    else tile_store_t<U, 2>(out_base, dt, nvalid, lds, lane, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -337,31 +555,46 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxArgs p) {
 }
 
 // Quantize: scale selection, encode, pack, dequantize, block error.
+// Each wave walks tiles of 64 units; lane l of a tile owns unit 64 t + l.
 template <class InT, int B, int H, int SF, int ST>
 __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs p) {
     constexpr int U = unit_elems<InT, B, H>();
     constexpr int NB = U / B;
+    constexpr int WAVE_LDS = kTileUnits * slot_bytes<U>();
+    __shared__ __attribute__((aligned(16))) char s_tiles[kThreads / 64][WAVE_LDS];
+    __shared__ BfTable s_bf;
+
     const InT* x = reinterpret_cast<const InT*>(p.x);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    char* lds = s_tiles[wave];
 
     const float g = workgroup_global_scale(p);
     if (blockIdx.x == 0 && threadIdx.x == 0 && p.g_out) *p.g_out = g;
     const float six_g = 6.0f * g, four_g = 4.0f * g;
+    if constexpr (ST == ST_BRUTE_FORCE) fill_bf_table<SF>(s_bf, g);
 
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < p.units; u += stride) {
-        const int64_t xo = unit_offset<U>(u, p.units_per_row, p.ld_x, p.contiguous);
+    const int64_t ntiles = (p.units + kTileUnits - 1) / kTileUnits;
+    const int64_t tstride = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < ntiles; t += tstride) {
+        const int64_t u0 = t * kTileUnits;
+        const int nvalid = (int)min<int64_t>(kTileUnits, p.units - u0);
+        const int64_t u = u0 + lane;
+        const bool active = lane < nvalid;
+
         float y[U];
-        load_elems<InT, U>(x + xo, y);
+        if (p.contiguous) {
+            tile_load<InT, U>(x + u0 * U, nvalid, lds, lane, y);
+        } else if (active) {
+            load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, false), y);
+        } else {
+#pragma unroll
+            for (int i = 0; i < U; ++i) y[i] = 0.0f;
+        }
         if constexpr (H > 0) fwht_segments<H, U>(y);
 
         uint32_t given[NB];
-        if constexpr (ST == ST_GIVEN) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) given[b] = p.scales[u * NB + b];
-        } else {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) given[b] = 0;
-        }
+        for (int b = 0; b < NB; ++b) given[b] = (ST == ST_GIVEN && active) ? p.scales[u * NB + b] : 0u;
 
         uint32_t code[U];
         float dq[U];
@@ -369,64 +602,78 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs p) {
         float sse[NB];
         static_for<NB>([&](auto bi) {
             constexpr int b = decltype(bi)::value;
-            quant_block<SF, ST, B, b>(y, g, six_g, four_g, p.prevent_zero, given[b], code, dq, sc[b], sse[b]);
+            quant_block<SF, ST, B, b>(y, g, six_g, four_g, p.prevent_zero, given[b], &s_bf, code, dq, sc[b], sse[b]);
         });
 
-        if (p.codes) store_codes<U>(p.codes + u * (U / 2), code);
-        if constexpr (ST != ST_GIVEN) {
+        if (active) {
+            if (p.codes) store_codes<U>(p.codes + u * (U / 2), code);
+            if constexpr (ST != ST_GIVEN) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) p.scales[u * NB + b] = (uint8_t)sc[b];
+                for (int b = 0; b < NB; ++b) p.scales[u * NB + b] = (uint8_t)sc[b];
+            }
+            if (p.sse) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) p.sse[u * NB + b] = sse[b];
+            }
+            if (p.mse) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const float m = sse[b] * (1.0f / (float)B);   // exact: B is a power of two
+                    p.mse[u * NB + b] = (m == m) ? m : as_f(kQNaN);
+                }
+            }
         }
         if (p.dq) {
-            const int64_t dqo = unit_offset<U>(u, p.units_per_row, p.ld_dq, p.contiguous);
-            store_elems_rt<U>(p.dq, p.dq_dt, dqo, dq);
-        }
-        if (p.sse) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) p.sse[u * NB + b] = sse[b];
-        }
-        if (p.mse) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float m = sse[b] * (1.0f / (float)B);   // exact: B is a power of two
-                p.mse[u * NB + b] = (m == m) ? m : as_f(kQNaN);
+            if (p.contiguous) {
+                const int eo = p.dq_dt == DT_F32 ? 4 : 2;
+                tile_store<U>(reinterpret_cast<char*>(p.dq) + u0 * U * eo, p.dq_dt, nvalid, lds, lane, dq);
+            } else if (active) {
+                store_elems_rt<U>(p.dq, p.dq_dt, unit_offset<U>(u, p.units_per_row, p.ld_dq, false), dq);
             }
         }
     }
 }
 
-// Dequantize codes + scales.
-template <int B>
+// Dequantize codes + scales.  One lane per DU consecutive output values
+// (DU = 8, or 4 when rows are not a multiple of 8 long): consecutive lanes
+// read consecutive code bytes and write consecutive output bytes.
+template <int B, int DU>
 __global__ __launch_bounds__(kThreads) void k_dequant(DequantArgs p) {
-    constexpr int U = cmax(B, 4);
-    constexpr int NB = U / B;
     const float g = read_g(p.g_dev);
+    const int64_t n = p.units;                        // rows * cols / DU
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < p.units; u += stride) {
-        uint32_t c[U];
-        load_codes<U>(p.codes + u * (U / 2), c);
-        float v[U];
+    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < n; j += stride) {
+        const int64_t e0 = j * DU;                    // flat element index (codes and scales are dense)
+        uint32_t c[DU];
+        load_codes<DU>(p.codes + e0 / 2, c);
+        constexpr int NBD = DU > B ? DU / B : 1;      // blocks touched by this lane
+        float S[NBD];
+        bool nan_block[NBD];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const uint32_t code = p.scales[u * NB + b];
-            float S;
-            bool nan_block;
+        for (int b = 0; b < NBD; ++b) {
+            const uint32_t code = p.scales[e0 / B + b];
             if (p.scale_fmt == SF_E8M0) {
-                nan_block = code == kE8M0NaN;
-                S = e8m0_value(code);
+                nan_block[b] = code == kE8M0NaN;
+                S[b] = e8m0_value(code);
             } else {
                 const uint32_t c7 = code & 0x7Fu;
-                S = e4m3_value(c7) * g;
-                nan_block = c7 == kE4M3NaN || !scale_usable(S);
-            }
-#pragma unroll
-            for (int i = 0; i < B; ++i) {
-                const uint32_t q = c[b * B + i];
-                const float sgn = as_f((q & 8u) << 28);
-                v[b * B + i] = nan_block ? canonical_nan_like(sgn) : with_sign_of(e2m1_value(q) * S, sgn);
+                S[b] = e4m3_value(c7) * g;
+                nan_block[b] = c7 == kE4M3NaN || !scale_usable(S[b]);
             }
         }
-        store_elems_rt<U>(p.out, p.out_dt, unit_offset<U>(u, p.units_per_row, p.ld_out, false), v);
+        float v[DU];
+#pragma unroll
+        for (int i = 0; i < DU; ++i) {
+            const int b = DU > B ? i / B : 0;
+            const float sgn = as_f((c[i] & 8u) << 28);
+            v[i] = nan_block[b] ? canonical_nan_like(sgn) : with_sign_of(e2m1_value(c[i]) * S[b], sgn);
+        }
+        int64_t off = e0;
+        if (p.ld_out != p.cols) {
+            const int64_t row = e0 / p.cols;
+            off = row * p.ld_out + (e0 - row * p.cols);
+        }
+        store_elems_rt<DU>(p.out, p.out_dt, off, v);
     }
 }
 
@@ -511,11 +758,13 @@ __global__ __launch_bounds__(kThreads) void k_relaxed_fwd(RelaxedArgs p) {
                 const float c_k = f16_value(p.c[row * nk + (col0 + b * B) / K + k]);
                 const float S_q = S_dq * c_k;
                 const bool ok = ok_dq && scale_usable(S_q);
+                const bool fast = fast_quotient_range(S_q);
+                const float R_q = fast ? 1.0f / S_q : 0.0f;
 #pragma unroll
                 for (int i = 0; i < K; ++i) {
                     const int j = b * B + k * K + i;
                     const float a = fabsf(y[j]);
-                    const float u_ = (S_q > 0.0f) ? a / S_q : 0.0f;
+                    const float u_ = fast ? quotient<SF_E4M3, true>(a, S_q, R_q) : quotient<SF_E4M3, false>(a, S_q, 0.0f);
                     float rr = e2m1_round(u_);
                     rr = (a == a) ? rr : 0.0f;
                     const uint32_t s = (as_u(y[j]) >> 31) << 3;
@@ -555,12 +804,15 @@ __global__ __launch_bounds__(kThreads) void k_relaxed_bwd(RelaxedArgs p) {
                 const float c_k = f16_value(p.c[ci]);
                 const float S_q = S_dq * c_k;
                 const bool ok = ok_dq && scale_usable(S_q);
+                const bool fast = fast_quotient_range(S_q);
+                const float R_q = fast ? 1.0f / S_q : 0.0f;
                 float t[K];
 #pragma unroll
                 for (int i = 0; i < K; ++i) {
                     const int j = b * B + k * K + i;
-                    bool inside = false;
-                    if (S_q > 0.0f) inside = fabsf(y[j]) / S_q <= 6.0f;
+                    const float a = fabsf(y[j]);
+                    const float u_ = fast ? quotient<SF_E4M3, true>(a, S_q, R_q) : quotient<SF_E4M3, false>(a, S_q, 0.0f);
+                    const bool inside = (S_q > 0.0f) && (u_ <= 6.0f);
                     t[i] = inside ? G[j] * y[j] : 0.0f;
                 }
                 const float A = tree_sum<K>(t);

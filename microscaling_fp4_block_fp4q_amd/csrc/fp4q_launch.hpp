@@ -15,7 +15,7 @@ hipError_t launch_quant_f16(const QuantArgs& a, int B, int H, int sf, int st, in
 
 hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t s);
 hipError_t launch_write_g(float* g_dev, float g, hipStream_t s);
-hipError_t launch_dequant(const DequantArgs& a, int B, int grid, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, int B, int DU, int grid, hipStream_t s);
 hipError_t launch_block_mse(const MseArgs& a, int x_dt, int B, int H, int grid, hipStream_t s);
 hipError_t launch_relaxed_fwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s);
 hipError_t launch_relaxed_bwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s);

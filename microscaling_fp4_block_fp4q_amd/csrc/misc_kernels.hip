@@ -33,15 +33,20 @@ hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_dequant(const DequantArgs& a, int B, int grid, hipStream_t s) {
+template <int DU>
+static hipError_t dequant_b(const DequantArgs& a, int B, int grid, hipStream_t s) {
     switch (B) {
-    case 4: hipLaunchKernelGGL(k_dequant<4>, dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(k_dequant<8>, dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL(k_dequant<16>, dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL(k_dequant<32>, dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_dequant<4, DU>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_dequant<8, DU>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_dequant<16, DU>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_dequant<32, DU>), dim3(grid), dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, int B, int DU, int grid, hipStream_t s) {
+    return DU == 8 ? dequant_b<8>(a, B, grid, s) : dequant_b<4>(a, B, grid, s);
 }
 
 template <class InT, int B>
