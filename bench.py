@@ -54,6 +54,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=12, help="rows per tensor in the oracle sample")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--only", default=None,
+                    help="profiling mode: run only the calls whose name contains one of these "
+                         "'|'-separated texts, --steps times, and print no result line")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="profiling mode: also run a device-to-device copy of this many MiB "
+                         "(calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -241,6 +247,25 @@ def main():
                 c.times.append((e0, e1))
             else:
                 c()
+
+    if args.only is not None or args.copy_mb:
+        pats = [] if args.only is None else args.only.split("|")
+        sel = [c for c in calls if any(pt in c.name for pt in pats)]
+        print(f"[bench] profiling {len(sel)} calls x {args.steps}: {[c.name for c in sel][:4]}", file=sys.stderr,
+              flush=True)
+        if args.copy_mb:
+            src = torch.empty(args.copy_mb << 18, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            src.fill_(1.0)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            for c in sel:
+                c()
+            if args.copy_mb:
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] profiling run done", file=sys.stderr, flush=True)
+        return
 
     print(f"[bench] {len(calls)} calls per step, warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -12,7 +12,7 @@ using namespace fp4q_dev;
 
 namespace {
 
-constexpr int kMaxGrid = 2048;   // workgroups of a grid-stride launch
+constexpr int kMaxGrid = 1 << 20;   // workgroups of a grid-stride launch (further capped by residency)
 
 int elem_size(int dt) { return dt == FP4Q_F32 ? 4 : 2; }
 bool dtype_ok(int dt) { return dt == FP4Q_F32 || dt == FP4Q_BF16 || dt == FP4Q_F16; }

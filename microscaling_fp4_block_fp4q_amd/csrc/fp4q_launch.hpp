@@ -20,11 +20,37 @@ hipError_t launch_block_mse(const MseArgs& a, int x_dt, int B, int H, int grid, 
 hipError_t launch_relaxed_fwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s);
 hipError_t launch_relaxed_bwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s);
 
+// Workgroups of KERNEL that the device holds at once (occupancy from its
+// registers and LDS, times the compute units), computed on first use.
+// Grid-stride kernels are launched with at most this many workgroups, so
+// every workgroup is resident from the start and the tiles are spread
+// evenly (a second, partial round of long-running workgroups would leave
+// most compute units idle at the end).
+template <auto KERNEL>
+int resident_workgroups() {
+    static const int n = [] {
+        int per_cu = 0, dev = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, kThreads, 0) != hipSuccess) per_cu = 1;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 256;
+        return (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    }();
+    return n;
+}
+
+template <auto KERNEL, class Args>
+hipError_t launch_resident(const Args& a, int grid, hipStream_t s) {
+    const int cap = resident_workgroups<KERNEL>();
+    hipLaunchKernelGGL(KERNEL, dim3(grid < cap ? grid : cap), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 // Template dispatch over block size, rotation size, scale format and strategy.
 template <class InT, int B, int H, int SF, int ST>
 hipError_t launch_quant_t(const QuantArgs& a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((k_quant<InT, B, H, SF, ST>), dim3(grid), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    if constexpr (ST == ST_BRUTE_FORCE) return launch_resident<k_quant_bf<InT, B, H, SF>>(a, grid, s);
+    else return launch_resident<k_quant<InT, B, H, SF, ST>>(a, grid, s);
 }
 
 template <class InT, int B, int H, int SF>

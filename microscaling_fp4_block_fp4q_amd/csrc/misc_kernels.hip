@@ -36,13 +36,12 @@ hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t
 template <int DU>
 static hipError_t dequant_b(const DequantArgs& a, int B, int grid, hipStream_t s) {
     switch (B) {
-    case 4: hipLaunchKernelGGL((k_dequant<4, DU>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_dequant<8, DU>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_dequant<16, DU>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_dequant<32, DU>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    case 4: return launch_resident<k_dequant<4, DU>>(a, grid, s);
+    case 8: return launch_resident<k_dequant<8, DU>>(a, grid, s);
+    case 16: return launch_resident<k_dequant<16, DU>>(a, grid, s);
+    case 32: return launch_resident<k_dequant<32, DU>>(a, grid, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_dequant(const DequantArgs& a, int B, int DU, int grid, hipStream_t s) {
@@ -52,12 +51,11 @@ hipError_t launch_dequant(const DequantArgs& a, int B, int DU, int grid, hipStre
 template <class InT, int B>
 static hipError_t mse_h(const MseArgs& a, int H, int grid, hipStream_t s) {
     switch (H) {
-    case 0: hipLaunchKernelGGL((k_block_mse<InT, B, 0>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_block_mse<InT, B, 16>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_block_mse<InT, B, 32>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    case 0: return launch_resident<k_block_mse<InT, B, 0>>(a, grid, s);
+    case 16: return launch_resident<k_block_mse<InT, B, 16>>(a, grid, s);
+    case 32: return launch_resident<k_block_mse<InT, B, 32>>(a, grid, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 template <class InT>
@@ -83,9 +81,8 @@ hipError_t launch_block_mse(const MseArgs& a, int x_dt, int B, int H, int grid, 
 template <bool BWD, class InT, int B, int K>
 static hipError_t relaxed_launch(const RelaxedArgs& a, int grid, hipStream_t s) {
     if constexpr (K <= B) {
-        if constexpr (BWD) hipLaunchKernelGGL((k_relaxed_bwd<InT, B, K>), dim3(grid), dim3(kThreads), 0, s, a);
-        else hipLaunchKernelGGL((k_relaxed_fwd<InT, B, K>), dim3(grid), dim3(kThreads), 0, s, a);
-        return hipGetLastError();
+        if constexpr (BWD) return launch_resident<k_relaxed_bwd<InT, B, K>>(a, grid, s);
+        else return launch_resident<k_relaxed_fwd<InT, B, K>>(a, grid, s);
     }
     return hipErrorInvalidValue;
 }
