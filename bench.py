@@ -39,9 +39,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, published
-VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # 256 CUs x 64 lanes x 2.4 GHz, one op per lane per clock
-BF_OPS_PER_EVAL = 13                       # VALU ops of one exact candidate-element evaluation (see design notes)
+HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, published
+VALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12   # 256 CUs x 128 fp32 lanes/clock x 2.4 GHz = 157.3 TFLOP/s / 2
+BF_INSTR_PER_EVAL = 13.25                   # VALU instructions of one candidate-element evaluation (B=16 loop)
+BF_CANDIDATES = 126                         # positive finite E4M3 scales an exhaustive search evaluates
+CSRC = os.path.join(ROOT, "microscaling_fp4_block_fp4q_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 STRATS = {0: "absmax", 1: "prevent-zero", 2: "4-over-6", 3: "brute-force"}
 
@@ -52,8 +55,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=12, help="rows per tensor in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="rows per tensor in the oracle sample")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--calls-out", default=None, help="write every call's mean time (ms) and bytes to this file")
+    ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR",
+                    help="summarise rocprofv3 csv output directories into --label under profiles/ and exit")
+    ap.add_argument("--label", default=None)
+    ap.add_argument("--command", default="", help="the command that produced the --summarize directories")
     ap.add_argument("--only", default=None,
                     help="profiling mode: run only the calls whose name contains one of these "
                          "'|'-separated texts, --steps times, and print no result line")
@@ -75,6 +83,91 @@ class Call:
         st = self.fn(*self.args)
         if st != 0:
             raise RuntimeError(f"{self.name}: status {st}")
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources and headers (ties counter profiles to a kernel version)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def summarize(dirs, label, command):
+    """Aggregate rocprofv3 csv output (kernel stats and counter collections)
+    into profiles/<label>.json (numbers) and profiles/<label>.md (table)."""
+    import csv
+    import glob
+    out = {"label": label, "command": command, "source_digest": source_digest(), "kernels": {}, "counters": {}}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                out["kernels"][r["Name"]] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                                             "min_us": float(r["MinNs"]) / 1e3,
+                                             "total_ms": float(r["TotalDurationNs"]) / 1e6,
+                                             "percent": float(r["Percentage"])}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            acc = {}
+            for r in csv.DictReader(open(f)):
+                acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            for k, cs in acc.items():
+                dst = out["counters"].setdefault(k, {})
+                for c, v in cs.items():
+                    dst[c] = {"mean": sum(v) / len(v), "dispatches": len(v)}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, label + ".json"), "w") as f:
+        json.dump(out, f, indent=1)
+    lines = [f"# {label}", "", f"Command: `{command}`", "", f"Kernel sources digest: `{out['source_digest']}`", ""]
+    if out["kernels"]:
+        lines += ["| kernel | calls | avg us | min us | total ms | % |", "|---|---|---|---|---|---|"]
+        for k, v in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["total_ms"])[:25]:
+            lines.append(f"| `{k[:90]}` | {v['calls']} | {v['avg_us']:.2f} | {v['min_us']:.2f} | "
+                         f"{v['total_ms']:.3f} | {v['percent']:.2f} |")
+        lines.append("")
+    if out["counters"]:
+        lines += ["| kernel | counter | mean per dispatch | dispatches |", "|---|---|---|---|"]
+        for k, cs in out["counters"].items():
+            for c, v in sorted(cs.items()):
+                lines.append(f"| `{k[:90]}` | {c} | {v['mean']:.1f} | {v['dispatches']} |")
+    with open(os.path.join(PROFILES, label + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote profiles/{label}.json and .md")
+
+
+def dominant_profile(kernel_name: str):
+    """Counters of kernel_name from the committed profile, or None when the
+    profile is missing or was taken on other kernel sources."""
+    path = os.path.join(PROFILES, "counters_bench_dominant.json")
+    if not os.path.exists(path):
+        return None
+    prof = json.load(open(path))
+    if prof.get("source_digest") != source_digest():
+        return None
+    return next((v for k, v in prof["counters"].items() if kernel_name in k), None)
+
+
+def counter_traffic(kernel_name: str):
+    """HBM bytes per launch of kernel_name from the committed counter profile,
+    scaled by a plain copy of known size; None if the profile is missing or
+    was taken on other kernel sources."""
+    path = os.path.join(PROFILES, "counters_bench_dominant.json")
+    if not os.path.exists(path):
+        return None
+    prof = json.load(open(path))
+    if prof.get("source_digest") != source_digest():
+        return None
+    cnt = prof["counters"]
+    copy = next((v for k, v in cnt.items() if "copyBuffer" in k), None)
+    kern = next((v for k, v in cnt.items() if kernel_name in k), None)
+    if not copy or not kern or "FETCH_SIZE" not in kern or "WRITE_SIZE" not in kern:
+        return None
+    copy_kib = prof.get("copy_mib", 256) * 1024.0
+    f_scale = copy_kib / copy["FETCH_SIZE"]["mean"]
+    w_scale = copy_kib / copy["WRITE_SIZE"]["mean"]
+    return 1024.0 * (kern["FETCH_SIZE"]["mean"] * f_scale + kern["WRITE_SIZE"]["mean"] * w_scale)
 
 
 def quant_bytes(rows, cols, B, in_es=4, dq_es=4, mse=True, dq=True):
@@ -102,11 +195,10 @@ def build_step(F, S, torch, dev):
 
     calls = []
     combos = [(B, st, gm) for B in (4, 8, 16, 32) for st in (0, 1, 2, 3) for gm in (1, 0)]
-    i = 0
-    for B, st, gm in combos:
-        for name in names:
-            x = X[names[(names.index(name) + i) % 4]]
-            i += 1
+    for ci, (B, st, gm) in enumerate(combos):
+        for ti in range(4):
+            tname = names[(ti + ci) % 4]       # every combo on all four tensors, rotated per combo
+            x = X[tname]
             cfg = F.config(F.E4M3, B, st, gm)
             keep.append(cfg)
             codes = t_empty((R, C // 2), torch.uint8)
@@ -119,7 +211,8 @@ def build_step(F, S, torch, dev):
                     F.F32, C, ptr(mse), ptr(ws), stream)
             calls.append(Call(f"quantize B={B} {STRATS[st]} {'amax' if gm else 'none'}", L.fp4q_quantize, args,
                               quant_bytes(R, C, B), R * C, "quantize",
-                              dict(B=B, strategy=STRATS[st], global_mode="tensor-amax" if gm else "none")))
+                              dict(B=B, strategy=STRATS[st], global_mode="tensor-amax" if gm else "none",
+                                   tensor=tname)))
 
     xn = X["normal"]
     # block Hadamard fused before quantization
@@ -220,6 +313,9 @@ def cpu_baseline(O, S, host, rows_per_tensor):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.label or "profile", args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no multi-GPU "
               "code: each GPU would quantize its own row shard independently).", file=sys.stderr)
@@ -299,17 +395,43 @@ def main():
                      "hbm_frac": round(b / (ms * 1e6) / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4)}
                  for k, (b, e, ms) in groups.items()}
 
-    # dominant kernel: the call family with the largest share of the step
-    bf = [(c, ms) for c, ms in per_call if c.meta.get("strategy") == "brute-force" and c.meta.get("global_mode") == "none"]
-    bf16 = [(c, ms) for c, ms in bf if c.meta["B"] == 16]
-    dom, dom_ms = bf16[0]
-    evals = 126 * dom.elems
-    achieved_tops = evals * BF_OPS_PER_EVAL / (dom_ms * 1e-3) / 1e12
-    roofline = {"bound": "alu", "kernel": "k_quant<float, B=16, H=0, E4M3, BRUTE_FORCE>",
-                "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s",
-                "frac": round(achieved_tops / VALU_PEAK_TOPS, 4), "traffic": None,
-                "avg_launch_ms": round(dom_ms, 4),
-                "work_per_launch": f"{evals} candidate-element evaluations x {BF_OPS_PER_EVAL} VALU ops"}
+    # dominant kernel: the kernel family (strategy, block) with the largest share of the step
+    fam = {}
+    for c, ms in per_call:
+        key = (c.meta.get("strategy", c.kind), c.meta.get("B"))
+        fam.setdefault(key, []).append((c, ms))
+    dom_key = max(fam, key=lambda k: sum(ms for _, ms in fam[k]))
+    dom = fam[dom_key]
+    solo = [(c, ms) for c, ms in dom if c.meta.get("global_mode") != "tensor-amax"] or dom
+    dom_ms = float(np.mean([ms for _, ms in solo]))    # launches without the abs-max pre-pass
+    dom_elems = dom[0][0].elems
+    strategy, B = dom_key
+    if strategy == "brute-force":
+        kname = f"k_quant_bf<float, {B}, 0, 1>"
+        work = BF_CANDIDATES * BF_INSTR_PER_EVAL * dom_elems          # exhaustive-search VALU work per launch
+        achieved = work / (dom_ms * 1e-3) / 1e12
+        roofline = {"bound": "alu", "kernel": kname, "achieved": round(achieved, 2),
+                    "peak": round(VALU_PEAK_TOPS, 1), "unit": "T VALU instr/s",
+                    "frac": round(achieved / VALU_PEAK_TOPS, 4),
+                    "work_per_launch": f"{BF_CANDIDATES} candidates x {BF_INSTR_PER_EVAL} VALU instructions x "
+                                       f"{dom_elems} elements (the exhaustive search; the exact branch and bound "
+                                       "evaluates a fraction of the candidates, so frac > 1 is pruning)",
+                    "avg_launch_ms": round(dom_ms, 4)}
+        prof = dominant_profile(kname)
+        if prof and "SQ_INSTS_VALU" in prof:
+            executed = prof["SQ_INSTS_VALU"]["mean"] * 64            # lane-instructions actually issued
+            roofline["executed_valu_instr_per_launch"] = round(executed)
+            roofline["executed_valu_frac"] = round(executed / (dom_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4)
+    else:
+        kname = f"k_quant<float, {B}" if B else dom[0][0].kind
+        nbytes = dom[0][0].nbytes
+        achieved = nbytes / (dom_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_launch_ms": round(dom_ms, 4)}
+    traffic = counter_traffic(kname)
+    roofline["traffic"] = None if traffic is None else round(traffic / 1e6, 2)
+    roofline["traffic_unit"] = "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roofline["algorithmic_MB_per_launch"] = round(dom[0][0].nbytes / 1e6, 2)
     stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
     sb = sum(c.nbytes for c, _ in stream_quant)
     sms = sum(ms for _, ms in stream_quant)
@@ -346,6 +468,10 @@ def main():
         result["cpu_baseline"] = {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                                   "sample": f"the step's call list on the first {args.cpu_rows} rows of each "
                                             f"4096x4096 tensor ({nb / 1e6:.1f} MB algorithmic, {dt:.1f} s)"}
+    if args.calls_out:
+        with open(args.calls_out, "w") as f:
+            json.dump([{"name": c.name, "tensor": c.meta.get("tensor"), "ms": ms, "bytes": c.nbytes}
+                       for c, ms in per_call], f, indent=0)
     line = json.dumps(result)
     print(line, flush=True)
     if args.json_out:

@@ -290,51 +290,102 @@ __device__ __forceinline__ unsigned long long pack_candidate(float sse, uint32_t
     return ((unsigned long long)as_u(sse) << 32) | code;
 }
 
+// First index in [lo, hi) where the monotone predicate (false ... true)
+// holds, or hi.  Starts at a guess and doubles its step outwards, so a good
+// guess costs two or three predicate evaluations; then bisects the bracket.
+template <class Pred>
+__device__ __forceinline__ uint32_t first_true_from(uint32_t lo, uint32_t hi, uint32_t guess, Pred pred) {
+    if (lo >= hi) return hi;
+    guess = guess < lo ? lo : (guess >= hi ? hi - 1 : guess);
+    uint32_t a, b;                        // pred(a - 1) false (or a == lo), pred(b) true (or b == hi)
+    if (pred(guess)) {
+        b = guess;
+        uint32_t step = 1;
+        a = lo;
+#pragma unroll 1
+        while (b > lo) {
+            const uint32_t c = b - lo > step ? b - step : lo;
+            if (!pred(c)) { a = c + 1; break; }
+            b = c;
+            step <<= 1;
+        }
+    } else {
+        a = guess + 1;
+        uint32_t step = 1;
+        b = hi;
+#pragma unroll 1
+        while (a < hi) {
+            const uint32_t c = hi - a > step ? a + step - 1 : hi - 1;
+            if (pred(c)) { b = c; break; }
+            a = c + 1;
+            step <<= 1;
+        }
+    }
+#pragma unroll 1
+    while (a < b) {
+        const uint32_t mid = (a + b) >> 1;
+        if (pred(mid)) b = mid; else a = mid + 1;
+    }
+    return a;
+}
+
 template <int SF, int B, int OFF, bool FAST, int U>
 __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], float a_b, uint32_t c_first,
-                                                        uint32_t c_second, const BfTable& t, uint32_t& c_lo,
-                                                        uint32_t& c_hi) {
+                                                        uint32_t c_second, float g, float six_g, const BfTable& t,
+                                                        uint32_t& c_lo, uint32_t& c_hi) {
     constexpr uint32_t CLO = SF == SF_E8M0 ? 0u : 1u;           // candidate codes [CLO, CEND)
     constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : 127u;
+    // every element encodes to zero at the smallest scale: all codes tie
+    if (a_b <= t.e[CLO].z) {
+        c_lo = c_hi = CLO;
+        return pack_candidate(0.0f, CLO);   // SSE of code CLO is re-computed by the final encode
+    }
     float rc[B];
     const float4 e1 = t.e[c_first], e2 = t.e[c_second];
     unsigned long long best = pack_candidate(encode_block<SF, B, OFF, false, FAST>(y, e1.x, e1.y, rc), c_first);
-    const unsigned long long b2 = pack_candidate(encode_block<SF, B, OFF, false, FAST>(y, e2.x, e2.y, rc), c_second);
-    best = b2 < best ? b2 : best;
+    if (c_second != c_first) {
+        const unsigned long long b2 =
+            pack_candidate(encode_block<SF, B, OFF, false, FAST>(y, e2.x, e2.y, rc), c_second);
+        best = b2 < best ? b2 : best;
+    }
     const float best0 = as_f((uint32_t)(best >> 32));
+    const uint32_t c_best = (uint32_t)(best & 0xFFFFFFFFull);
 
+    // fl(6 S_c), computed the way the encoder computes it (grid value 6 times S_c)
+    auto six_s = [&](uint32_t c) {
+        if constexpr (SF == SF_E8M0) return 6.0f * e8m0_value(c);
+        else return 6.0f * (e4m3_value(c) * g);
+    };
+
+    // upper end: first code past c_best whose zero-bin bound exceeds best0, or
+    // whose every element encodes to zero (that code is still evaluated)
     float sq[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) sq[i] = y[OFF + i] * y[OFF + i];
-    uint32_t lo = CLO, hi = CEND;
-#pragma unroll 1
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        const float T0 = t.e[mid].z;
+    auto stop_up = [&](uint32_t c) {
+        const float T0 = t.e[c].z;
         float z[B];
 #pragma unroll
         for (int i = 0; i < B; ++i) z[i] = fabsf(y[OFF + i]) <= T0 ? sq[i] : 0.0f;
-        const bool stop = tree_sum<B>(z) > best0 || a_b <= T0;
-        if (stop) hi = mid; else lo = mid + 1;
-    }
-    c_hi = lo;                                           // first code that stops the scan
-    if (c_hi < CEND && a_b <= t.e[c_hi].z) ++c_hi;       // the all-zero code itself may still win a tie
+        return tree_sum<B>(z) > best0 || a_b <= T0;
+    };
+    uint32_t guess_hi;
+    if constexpr (SF == SF_E8M0) guess_hi = c_best + 3u;
+    else guess_hi = e4m3_encode(a_b / g) + 16u;           // around where a_max / S drops near 0.25 * 4
+    c_hi = first_true_from(c_best + 1u, CEND, guess_hi, stop_up);
+    if (c_hi < CEND && a_b <= t.e[c_hi].z) ++c_hi;
 
-    lo = CLO; hi = CEND;
-#pragma unroll 1
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (t.e[mid].w > a_b) hi = mid; else lo = mid + 1;
-    }
-    const uint32_t c_star = lo;                          // first code with fl(6 S) > a_max
-    lo = CLO; hi = c_star;
-#pragma unroll 1
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        const float d = a_b - t.e[mid].w;
-        if (d * d <= best0) hi = mid; else lo = mid + 1;
-    }
-    c_lo = lo;
+    // lower end: below c_star the block maximum saturates (fl(6 S) <= a_max) and
+    // contributes (a_max - fl(6 S))^2; skip the codes where that exceeds best0
+    const uint32_t c_star = first_true_from(CLO, CEND, c_first, [&](uint32_t c) { return six_s(c) > a_b; });
+    auto keep_lo = [&](uint32_t c) {
+        const float d = a_b - six_s(c);
+        return d * d <= best0;
+    };
+    uint32_t guess_lo;
+    if constexpr (SF == SF_E8M0) guess_lo = c_star > CLO ? c_star - 1u : CLO;
+    else guess_lo = e4m3_encode(fmaxf(a_b - __builtin_sqrtf(best0), 0.0f) / six_g);
+    c_lo = first_true_from(CLO, c_star, guess_lo, keep_lo);
     return best;
 }
 
@@ -740,8 +791,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                     c2 = s4 > 0u ? s4 : 1u;
                 }
                 uint32_t lo, hi;
-                if (fast) best = bf_window<SF, B, b * B, true>(y, a_b, c1, c2, s_bf, lo, hi);
-                else best = bf_window<SF, B, b * B, false>(y, a_b, c1, c2, s_bf, lo, hi);
+                if (fast) best = bf_window<SF, B, b * B, true>(y, a_b, c1, c2, g, six_g, s_bf, lo, hi);
+                else best = bf_window<SF, B, b * B, false>(y, a_b, c1, c2, g, six_g, s_bf, lo, hi);
                 clo[b] = lo;
                 n[b] = hi > lo ? hi - lo : 0u;
             }
@@ -784,16 +835,20 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                 }
             };
             load_block(k);
+            uint32_t k_begin = W.start[k], k_end = W.start[k + 1], k_clo = W.clo[k];
             unsigned long long local = ~0ull;
 #pragma unroll 1
             for (uint32_t j = j0; j < j1; ++j) {
-                while (j >= W.start[k + 1]) {
+                while (j >= k_end) {
                     atomicMin(&W.best[k], local);
                     local = ~0ull;
                     ++k;
-                    load_block(k);
+                    k_begin = k_end;
+                    k_end = W.start[k + 1];
+                    k_clo = W.clo[k];
+                    if (j < k_end) load_block(k);
                 }
-                const uint32_t c = W.clo[k] + (j - W.start[k]);
+                const uint32_t c = k_clo + (j - k_begin);
                 const float4 e = s_bf.e[c];
                 float rc[B];
                 float sse;
