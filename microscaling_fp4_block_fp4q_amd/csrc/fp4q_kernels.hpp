@@ -234,8 +234,9 @@ __device__ __forceinline__ float encode_block_e4m3(const float (&y)[U], float S,
 //   fl(a / S_c) <= 0.25 (a that encodes to zero),  w = fl(6 S_c), the value a
 //   saturated element dequantizes to.
 struct BfTable {
-    float4 e[256];
-    bool fast;   // every candidate in the division-free range
+    float2 sr[256];   // (S_c, R_c)
+    float t0[256];    // T0_c
+    bool fast;        // every candidate in the division-free range
 };
 
 // Largest fp32 a with a / S <= 0.25 + 2^-26 (the rounding boundary above
@@ -260,7 +261,8 @@ __device__ __forceinline__ void fill_bf_table(BfTable& t, float g) {
             S = e4m3_value(c) * g;
             R = fast_quotient_range(S) ? 1.0f / S : 0.0f;
         }
-        t.e[c] = make_float4(S, R, zero_bin_limit(S), 6.0f * S);
+        t.sr[c] = make_float2(S, R);
+        t.t0[c] = zero_bin_limit(S);
     }
     if (threadIdx.x == 0)
         t.fast = SF == SF_E8M0 || (fast_quotient_range(e4m3_value(1u) * g) && fast_quotient_range(e4m3_value(0x7Eu) * g));
@@ -336,12 +338,12 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
     constexpr uint32_t CLO = SF == SF_E8M0 ? 0u : 1u;           // candidate codes [CLO, CEND)
     constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : 127u;
     // every element encodes to zero at the smallest scale: all codes tie
-    if (a_b <= t.e[CLO].z) {
+    if (a_b <= t.t0[CLO]) {
         c_lo = c_hi = CLO;
         return pack_candidate(0.0f, CLO);   // SSE of code CLO is re-computed by the final encode
     }
     float rc[B];
-    const float4 e1 = t.e[c_first], e2 = t.e[c_second];
+    const float2 e1 = t.sr[c_first], e2 = t.sr[c_second];
     unsigned long long best = pack_candidate(encode_block<SF, B, OFF, false, FAST>(y, e1.x, e1.y, rc), c_first);
     if (c_second != c_first) {
         const unsigned long long b2 =
@@ -363,7 +365,7 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
 #pragma unroll
     for (int i = 0; i < B; ++i) sq[i] = y[OFF + i] * y[OFF + i];
     auto stop_up = [&](uint32_t c) {
-        const float T0 = t.e[c].z;
+        const float T0 = t.t0[c];
         float z[B];
 #pragma unroll
         for (int i = 0; i < B; ++i) z[i] = fabsf(y[OFF + i]) <= T0 ? sq[i] : 0.0f;
@@ -373,7 +375,7 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
     if constexpr (SF == SF_E8M0) guess_hi = c_best + 3u;
     else guess_hi = e4m3_encode(a_b / g) + 16u;           // around where a_max / S drops near 0.25 * 4
     c_hi = first_true_from(c_best + 1u, CEND, guess_hi, stop_up);
-    if (c_hi < CEND && a_b <= t.e[c_hi].z) ++c_hi;
+    if (c_hi < CEND && a_b <= t.t0[c_hi]) ++c_hi;
 
     // lower end: below c_star the block maximum saturates (fl(6 S) <= a_max) and
     // contributes (a_max - fl(6 S))^2; skip the codes where that exceeds best0
@@ -390,11 +392,38 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
 }
 
 // Scale selection + encoding of block number BI of a unit.
-template <int SF, int ST, int B, int BI, int U>
+constexpr int code_words(int U) { return (U + 7) / 8; }
+
+// Pack the codes of block OFF/B into the unit's code words and hand its
+// dequantized values (fp32) to emit(off, values), four at a time.
+template <int B, int OFF, int U, class Emit>
+__device__ __forceinline__ void finish_block(const float (&y)[U], const float (&r)[B], float S, bool nan_block,
+                                             uint32_t (&cw)[code_words(U)], Emit&& emit) {
+#pragma unroll
+    for (int i0 = 0; i0 < B; i0 += 4) {
+        float dq4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + k;
+            const uint32_t sgn = as_u(y[OFF + i]) >> 31;
+            uint32_t nib;
+            if (nan_block) {
+                nib = sgn << 3;
+                dq4[k] = canonical_nan_like(y[OFF + i]);
+            } else {
+                nib = (sgn << 3) | e2m1_code_of(r[i]);
+                dq4[k] = with_sign_of(r[i] * S, y[OFF + i]);
+            }
+            cw[(OFF + i) / 8] |= nib << (4 * ((OFF + i) % 8));
+        }
+        emit(OFF + i0, dq4);
+    }
+}
+
+template <int SF, int ST, int B, int BI, int U, class Emit>
 __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float six_g, float four_g,
-                                            int prevent_zero, uint32_t given,
-                                            uint32_t (&code)[U], float (&dq)[U], uint32_t& scale_code,
-                                            float& sse) {
+                                            int prevent_zero, uint32_t given, uint32_t (&cw)[code_words(U)],
+                                            Emit&& emit, uint32_t& scale_code, float& sse) {
     constexpr int OFF = BI * B;
     uint32_t sc;
     bool nan_block;
@@ -434,15 +463,14 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
                     static_assert(ST == ST_FOUR_OVER_SIX, "brute force has its own kernel");
                     const uint32_t s4 = e4m3_encode(a_b / four_g);
                     const float S6 = e4m3_value(s6) * g, S4 = e4m3_value(s4) * g;
-                    float r4[B];
+                    // score both candidates, then encode the winner again: cheaper in
+                    // registers than holding two rounded blocks
                     const float e6 = encode_block_e4m3<B, OFF, false>(y, S6, r);
-                    const float e4 = encode_block_e4m3<B, OFF, false>(y, S4, r4);
+                    const float e4 = encode_block_e4m3<B, OFF, false>(y, S4, r);
                     const bool take4 = e4 < e6;   // equal error keeps the smaller code s6
                     sc = take4 ? s4 : s6;
                     S = take4 ? S4 : S6;
-                    sse = take4 ? e4 : e6;
-#pragma unroll
-                    for (int i = 0; i < B; ++i) r[i] = take4 ? r4[i] : r[i];
+                    sse = encode_block_e4m3<B, OFF, false>(y, S, r);
                 }
             }
         } else {
@@ -451,20 +479,8 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
     }
 
     scale_code = sc;
-    if (nan_block) {
-        sse = as_f(kQNaN);
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-            code[OFF + i] = (as_u(y[OFF + i]) >> 31) << 3;
-            dq[OFF + i] = canonical_nan_like(y[OFF + i]);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-            code[OFF + i] = ((as_u(y[OFF + i]) >> 31) << 3) | e2m1_code_of(r[i]);
-            dq[OFF + i] = with_sign_of(r[i] * S, y[OFF + i]);
-        }
-    }
+    if (nan_block) sse = as_f(kQNaN);
+    finish_block<B, OFF>(y, r, S, nan_block, cw, emit);
 }
 
 // ---------------------------------------------------------------------------
@@ -512,18 +528,16 @@ __device__ __forceinline__ void tile_load(const T* __restrict__ base, int nvalid
     wave_sync_lds();
 }
 
-// Store the lanes' U values (as type dt) of a tile of nvalid units to
-// out_base, coalesced.
+// Copy a tile of nvalid units whose values (type of size EO) sit in the
+// lanes' LDS slots to out_base, 16 coalesced bytes per lane.
 template <int U, int EO>
-__device__ __forceinline__ void tile_store_t(void* __restrict__ out_base, int dt, int nvalid, char* lds, int lane,
-                                             const float (&v)[U]) {
-    constexpr int BYTES = U * EO;
-    if constexpr (BYTES >= 16) {
-        constexpr int C = BYTES / 16;
-        constexpr int SLOT = slot_bytes<U>();
-        store_elems_rt<U>(lds + lane * SLOT, dt, 0, v);
-        wave_sync_lds();
-        uint4* dst = reinterpret_cast<uint4*>(out_base);
+__device__ __forceinline__ void tile_flush_t(void* __restrict__ out_base, int nvalid, const char* lds, int lane) {
+    constexpr int UB = U * EO;                 // bytes of one unit
+    constexpr int SLOT = slot_bytes<U>();
+    uint4* dst = reinterpret_cast<uint4*>(out_base);
+    wave_sync_lds();
+    if constexpr (UB >= 16) {
+        constexpr int C = UB / 16;
         const int nchunks = nvalid * C;
 #pragma unroll
         for (int k = 0; k < C; ++k) {
@@ -531,17 +545,56 @@ __device__ __forceinline__ void tile_store_t(void* __restrict__ out_base, int dt
             if (j < nchunks) dst[j] = *reinterpret_cast<const uint4*>(lds + (j / C) * SLOT + (j % C) * 16);
         }
     } else {
-        // 8-byte units (4 values of 2 bytes): already contiguous per lane
-        if (lane < nvalid) store_elems_rt<U>(out_base, dt, (int64_t)lane * U, v);
+        static_assert(UB == 8, "units of 4 two-byte values");
+        const int nchunks = nvalid / 2;        // pairs of units
+        if (lane < nchunks) {
+            const uint2 a = *reinterpret_cast<const uint2*>(lds + (2 * lane) * SLOT);
+            const uint2 b = *reinterpret_cast<const uint2*>(lds + (2 * lane + 1) * SLOT);
+            dst[lane] = make_uint4(a.x, a.y, b.x, b.y);
+        }
+        if ((nvalid & 1) && lane == nvalid - 1)
+            reinterpret_cast<uint2*>(out_base)[lane] = *reinterpret_cast<const uint2*>(lds + lane * SLOT);
     }
     wave_sync_lds();
 }
 
 template <int U>
-__device__ __forceinline__ void tile_store(void* __restrict__ out_base, int dt, int nvalid, char* lds, int lane,
-                                           const float (&v)[U]) {
-    if (dt == DT_F32) tile_store_t<U, 4>(out_base, dt, nvalid, lds, lane, v);
-    else tile_store_t<U, 2>(out_base, dt, nvalid, lds, lane, v);
+__device__ __forceinline__ void tile_flush(void* __restrict__ out_base, int dt, int nvalid, const char* lds, int lane) {
+    if (dt == DT_F32) tile_flush_t<U, 4>(out_base, nvalid, lds, lane);
+    else tile_flush_t<U, 2>(out_base, nvalid, lds, lane);
+}
+
+// Store U/2 packed code bytes from code words.
+template <int U>
+__device__ __forceinline__ void store_code_words(uint8_t* __restrict__ p, const uint32_t (&cw)[code_words(U)]) {
+    if constexpr (U == 32) *reinterpret_cast<uint4*>(p) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    else if constexpr (U == 16) *reinterpret_cast<uint2*>(p) = make_uint2(cw[0], cw[1]);
+    else if constexpr (U == 8) *reinterpret_cast<uint32_t*>(p) = cw[0];
+    else *reinterpret_cast<uint16_t*>(p) = (uint16_t)cw[0];
+}
+
+// Destination of a unit's dequantized values: the lane's LDS slot when the
+// tile is flushed coalesced afterwards (contiguous tensors), else the strided
+// output itself.  Kept as two pointers so that each store keeps its address
+// space.
+template <int U>
+struct DqSink {
+    char* slot;          // LDS slot, or null
+    void* out;           // global output, or null
+    int64_t off;         // element offset of the unit in out
+    int dt;
+    __device__ __forceinline__ void operator()(int o, const float (&v)[4]) const {
+        if (slot) store_elems_rt<4>(slot, dt, o, v);
+        else if (out) store_elems_rt<4>(out, dt, off + o, v);
+    }
+};
+
+template <int U, class P>
+__device__ __forceinline__ DqSink<U> dq_sink(const P& p, char* lds, int lane, int64_t u, bool active) {
+    if (!p.dq) return {nullptr, nullptr, 0, 0};
+    if (p.contiguous) return {lds + lane * slot_bytes<U>(), nullptr, 0, p.dq_dt};
+    if (!active) return {nullptr, nullptr, 0, 0};
+    return {nullptr, p.dq, unit_offset<U>(u, p.units_per_row, p.ld_dq, false), p.dq_dt};
 }
 
 // ---------------------------------------------------------------------------
@@ -621,54 +674,32 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs p) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) given[b] = (ST == ST_GIVEN && active) ? p.scales[u * NB + b] : 0u;
 
-        uint32_t code[U];
-        float dq[U];
+        uint32_t cw[code_words(U)];
+#pragma unroll
+        for (int i = 0; i < code_words(U); ++i) cw[i] = 0;
+        const DqSink<U> sink = dq_sink<U>(p, lds, lane, u, active);
         uint32_t sc[NB];
         float sse[NB];
         static_for<NB>([&](auto bi) {
             constexpr int b = decltype(bi)::value;
-            quant_block<SF, ST, B, b>(y, g, six_g, four_g, p.prevent_zero, given[b], code, dq, sc[b], sse[b]);
+            quant_block<SF, ST, B, b>(y, g, six_g, four_g, p.prevent_zero, given[b], cw, sink, sc[b], sse[b]);
         });
-
-        if (active) {
-            if (p.codes) store_codes<U>(p.codes + u * (U / 2), code);
-            if constexpr (ST != ST_GIVEN) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) p.scales[u * NB + b] = (uint8_t)sc[b];
-            }
-            if (p.sse) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) p.sse[u * NB + b] = sse[b];
-            }
-            if (p.mse) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const float m = sse[b] * (1.0f / (float)B);   // exact: B is a power of two
-                    p.mse[u * NB + b] = (m == m) ? m : as_f(kQNaN);
-                }
-            }
-        }
-        if (p.dq) {
-            if (p.contiguous) {
-                const int eo = p.dq_dt == DT_F32 ? 4 : 2;
-                tile_store<U>(reinterpret_cast<char*>(p.dq) + u0 * U * eo, p.dq_dt, nvalid, lds, lane, dq);
-            } else if (active) {
-                store_elems_rt<U>(p.dq, p.dq_dt, unit_offset<U>(u, p.units_per_row, p.ld_dq, false), dq);
-            }
-        }
+        store_unit_outputs<B, U>(p, u0, nvalid, lane, lds, cw, sc, sse, ST != ST_GIVEN);
     }
 }
 
-// Outputs of one tile (codes, scales, SSE, MSE, dequantized values).
+// Outputs of one tile: codes, scales, SSE and MSE from the lanes' registers;
+// the dequantized values, already in the LDS slots for contiguous tensors,
+// are flushed coalesced.
 template <int B, int U>
-__device__ __forceinline__ void store_unit_outputs(const QuantArgs& p, int64_t u0, int nvalid, int lane, char* lds,
-                                                   const uint32_t (&code)[U], const float (&dq)[U],
+__device__ __forceinline__ void store_unit_outputs(const QuantArgs& p, int64_t u0, int nvalid, int lane,
+                                                   const char* lds, const uint32_t (&cw)[code_words(U)],
                                                    const uint32_t (&sc)[U / B], const float (&sse)[U / B],
                                                    bool write_scales) {
     constexpr int NB = U / B;
     const int64_t u = u0 + lane;
     if (lane < nvalid) {
-        if (p.codes) store_codes<U>(p.codes + u * (U / 2), code);
+        if (p.codes) store_code_words<U>(p.codes + u * (U / 2), cw);
         if (write_scales) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) p.scales[u * NB + b] = (uint8_t)sc[b];
@@ -685,13 +716,9 @@ __device__ __forceinline__ void store_unit_outputs(const QuantArgs& p, int64_t u
             }
         }
     }
-    if (p.dq) {
-        if (p.contiguous) {
-            const int eo = p.dq_dt == DT_F32 ? 4 : 2;
-            tile_store<U>(reinterpret_cast<char*>(p.dq) + u0 * U * eo, p.dq_dt, nvalid, lds, lane, dq);
-        } else if (lane < nvalid) {
-            store_elems_rt<U>(p.dq, p.dq_dt, unit_offset<U>(u, p.units_per_row, p.ld_dq, false), dq);
-        }
+    if (p.dq && p.contiguous) {
+        const int eo = p.dq_dt == DT_F32 ? 4 : 2;
+        tile_flush<U>(reinterpret_cast<char*>(p.dq) + u0 * U * eo, p.dq_dt, nvalid, lds, lane);
     }
 }
 
@@ -825,16 +852,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                 if (W.start[mid] <= j0) lo = mid; else hi = mid - 1;
             }
             uint32_t k = lo;
-            float yb[B];
-            auto load_block = [&](uint32_t kk) {
+            auto load_block = [&](uint32_t kk, float (&dst)[B]) {
                 const float4* src = reinterpret_cast<const float4*>(W.tile + (kk / NB) * SLOT + (kk % NB) * B * 4);
 #pragma unroll
                 for (int i = 0; i < B / 4; ++i) {
                     const float4 v = src[i];
-                    yb[4 * i] = v.x; yb[4 * i + 1] = v.y; yb[4 * i + 2] = v.z; yb[4 * i + 3] = v.w;
+                    dst[4 * i] = v.x; dst[4 * i + 1] = v.y; dst[4 * i + 2] = v.z; dst[4 * i + 3] = v.w;
                 }
             };
-            load_block(k);
+            float yb[B];
+            load_block(k, yb);
             uint32_t k_begin = W.start[k], k_end = W.start[k + 1], k_clo = W.clo[k];
             unsigned long long local = ~0ull;
 #pragma unroll 1
@@ -846,10 +873,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                     k_begin = k_end;
                     k_end = W.start[k + 1];
                     k_clo = W.clo[k];
-                    if (j < k_end) load_block(k);
+                    if (j < k_end) load_block(k, yb);
                 }
                 const uint32_t c = k_clo + (j - k_begin);
-                const float4 e = s_bf.e[c];
+                const float2 e = s_bf.sr[c];
                 float rc[B];
                 float sse;
                 if (fast) sse = encode_block<SF, B, 0, false, true>(yb, e.x, e.y, rc);
@@ -862,42 +889,36 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
         wave_sync_lds();
 
         // encode every block at its winning code
-        uint32_t code[U];
-        float dq[U];
+        uint32_t cw[code_words(U)];
+#pragma unroll
+        for (int i = 0; i < code_words(U); ++i) cw[i] = 0;
+        const DqSink<U> sink = dq_sink<U>(p, W.tile, lane, u, active);
         uint32_t sc[NB];
         float sse[NB];
         static_for<NB>([&](auto bi) {
             constexpr int b = decltype(bi)::value;
             constexpr int OFF = b * B;
             float r[B];
+            float S = 0.0f;
             if (nan_blk[b]) {
                 sc[b] = SF == SF_E8M0 ? kE8M0NaN : kE4M3NaN;
                 sse[b] = as_f(kQNaN);
 #pragma unroll
-                for (int i = 0; i < B; ++i) {
-                    code[OFF + i] = (as_u(y[OFF + i]) >> 31) << 3;
-                    dq[OFF + i] = canonical_nan_like(y[OFF + i]);
-                }
+                for (int i = 0; i < B; ++i) r[i] = 0.0f;
             } else {
                 const uint32_t c = (uint32_t)(W.best[lane * NB + b] & 0xFFFFFFFFull) % CEND;
                 sc[b] = c;
-                float S;
                 if constexpr (SF == SF_E8M0) {
                     S = e8m0_value(c);
                     sse[b] = encode_block<SF, B, OFF, false, true>(y, S, e8m0_inverse(c), r);
                 } else {
-                    S = s_bf.e[c].x;
+                    S = s_bf.sr[c].x;
                     sse[b] = encode_block_e4m3<B, OFF, false>(y, S, r);
                 }
-#pragma unroll
-                for (int i = 0; i < B; ++i) {
-                    code[OFF + i] = ((as_u(y[OFF + i]) >> 31) << 3) | e2m1_code_of(r[i]);
-                    dq[OFF + i] = with_sign_of(r[i] * S, y[OFF + i]);
-                }
             }
+            finish_block<B, OFF>(y, r, S, nan_blk[b], cw, sink);
         });
-        wave_sync_lds();
-        store_unit_outputs<B, U>(p, u0, nvalid, lane, W.tile, code, dq, sc, sse, true);
+        store_unit_outputs<B, U>(p, u0, nvalid, lane, W.tile, cw, sc, sse, true);
     }
 }
 
