@@ -234,9 +234,10 @@ __device__ __forceinline__ float encode_block_e4m3(const float (&y)[U], float S,
 //   fl(a / S_c) <= 0.25 (a that encodes to zero),  w = fl(6 S_c), the value a
 //   saturated element dequantizes to.
 struct BfTable {
-    float2 sr[256];   // (S_c, R_c)
-    float t0[256];    // T0_c
-    bool fast;        // every candidate in the division-free range
+    static constexpr int kPad = 8;   // entries past the last code, read by padded work items
+    float2 sr[256 + kPad];           // (S_c, R_c)
+    float t0[256];                   // T0_c
+    bool fast;                       // every candidate in the division-free range
 };
 
 // Largest fp32 a with a / S <= 0.25 + 2^-26 (the rounding boundary above
@@ -264,6 +265,9 @@ __device__ __forceinline__ void fill_bf_table(BfTable& t, float g) {
         t.sr[c] = make_float2(S, R);
         t.t0[c] = zero_bin_limit(S);
     }
+    // codes past the last one: harmless values for work items padded to a
+    // whole number of candidates (their results are discarded)
+    for (uint32_t c = N + threadIdx.x; c < 256u + BfTable::kPad; c += kThreads) t.sr[c] = make_float2(1.0f, 1.0f);
     if (threadIdx.x == 0)
         t.fast = SF == SF_E8M0 || (fast_quotient_range(e4m3_value(1u) * g) && fast_quotient_range(e4m3_value(0x7Eu) * g));
     __syncthreads();
@@ -463,14 +467,15 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
                     static_assert(ST == ST_FOUR_OVER_SIX, "brute force has its own kernel");
                     const uint32_t s4 = e4m3_encode(a_b / four_g);
                     const float S6 = e4m3_value(s6) * g, S4 = e4m3_value(s4) * g;
-                    // score both candidates, then encode the winner again: cheaper in
-                    // registers than holding two rounded blocks
+                    float r4[B];
                     const float e6 = encode_block_e4m3<B, OFF, false>(y, S6, r);
-                    const float e4 = encode_block_e4m3<B, OFF, false>(y, S4, r);
+                    const float e4 = encode_block_e4m3<B, OFF, false>(y, S4, r4);
                     const bool take4 = e4 < e6;   // equal error keeps the smaller code s6
                     sc = take4 ? s4 : s6;
                     S = take4 ? S4 : S6;
-                    sse = encode_block_e4m3<B, OFF, false>(y, S, r);
+                    sse = take4 ? e4 : e6;
+#pragma unroll
+                    for (int i = 0; i < B; ++i) r[i] = take4 ? r4[i] : r[i];
                 }
             }
         } else {
@@ -736,10 +741,13 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 // Per tile: each lane publishes its (rotated) fp32 values in LDS and finds,
 // for each of its blocks, the best of two start scales and the window of
 // codes that can still beat it (bf_window).  The windows of all blocks of the
-// tile form one work list that the 64 lanes split evenly: a lane walks its
-// slice, evaluates (block, code) pairs with the block's values read from LDS,
-// and merges its per-block minimum into an LDS 64-bit atomic minimum over
-// (SSE bits, code).  Then every lane encodes its blocks at the winning code.
+// tile form one work list that the 64 lanes split evenly: a work item is K
+// consecutive codes of one block (K = 16 / B for small blocks, which gives a
+// lane independent candidates to interleave; a window is padded to whole
+// items and the padding discarded).  A lane walks its slice, evaluates the
+// items with the block's values read from LDS, and merges its per-block
+// minimum into an LDS 64-bit atomic minimum over (SSE bits, code).  Then
+// every lane encodes its blocks at the winning code.
 template <class InT, int B, int H, int SF>
 __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
     constexpr int U = unit_elems<InT, B, H>();
@@ -747,11 +755,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
     constexpr int SLOT = slot_bytes<U>();
     constexpr int NBLK = kTileUnits * NB;
     constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : 127u;
+    constexpr int K = B >= 16 ? 1 : 16 / B;       // candidates of one block per work item
+    // an item reads codes c0 .. c0 + K - 1 with c0 < CEND
+    static_assert(CEND + K - 1 <= 256 + BfTable::kPad, "items read past the table");
     struct WaveLds {
         char tile[kTileUnits * SLOT];
         unsigned long long best[NBLK];
         uint32_t start[NBLK + 1];
         uint8_t clo[NBLK];
+        uint8_t chi[NBLK];
     };
     __shared__ __attribute__((aligned(16))) WaveLds s_w[kThreads / 64];
     __shared__ BfTable s_bf;
@@ -795,7 +807,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             reinterpret_cast<float4*>(W.tile + lane * SLOT)[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
 
         // start candidates and windows of this lane's blocks
-        uint32_t n[NB], clo[NB];
+        uint32_t n[NB], clo[NB], chi[NB];
         bool nan_blk[NB];
         static_for<NB>([&](auto bi) {
             constexpr int b = decltype(bi)::value;
@@ -805,6 +817,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             nan_blk[b] = ab >= 0x7F800000u || !(g < __builtin_inff());
             n[b] = 0;
             clo[b] = 0;
+            chi[b] = 0;
             unsigned long long best = ~0ull;
             if (!nan_blk[b] && active) {
                 const float a_b = as_f(ab);
@@ -821,7 +834,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                 if (fast) best = bf_window<SF, B, b * B, true>(y, a_b, c1, c2, g, six_g, s_bf, lo, hi);
                 else best = bf_window<SF, B, b * B, false>(y, a_b, c1, c2, g, six_g, s_bf, lo, hi);
                 clo[b] = lo;
-                n[b] = hi > lo ? hi - lo : 0u;
+                chi[b] = hi;
+                n[b] = hi > lo ? (hi - lo + K - 1) / K : 0u;     // work items of K codes
             }
             W.best[lane * NB + b] = best;
         });
@@ -837,6 +851,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
         for (int b = 0; b < NB; ++b) {
             W.start[lane * NB + b] = run;
             W.clo[lane * NB + b] = (uint8_t)clo[b];
+            W.chi[lane * NB + b] = (uint8_t)chi[b];
             run += n[b];
         }
         if (lane == 63) W.start[NBLK] = total;
@@ -862,7 +877,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             };
             float yb[B];
             load_block(k, yb);
-            uint32_t k_begin = W.start[k], k_end = W.start[k + 1], k_clo = W.clo[k];
+            uint32_t k_begin = W.start[k], k_end = W.start[k + 1], k_clo = W.clo[k], k_chi = W.chi[k];
             unsigned long long local = ~0ull;
 #pragma unroll 1
             for (uint32_t j = j0; j < j1; ++j) {
@@ -873,16 +888,23 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                     k_begin = k_end;
                     k_end = W.start[k + 1];
                     k_clo = W.clo[k];
+                    k_chi = W.chi[k];
                     if (j < k_end) load_block(k, yb);
                 }
-                const uint32_t c = k_clo + (j - k_begin);
-                const float2 e = s_bf.sr[c];
-                float rc[B];
-                float sse;
-                if (fast) sse = encode_block<SF, B, 0, false, true>(yb, e.x, e.y, rc);
-                else sse = encode_block<SF, B, 0, false, false>(yb, e.x, e.y, rc);
-                const unsigned long long cand = pack_candidate(sse, c);
-                local = cand < local ? cand : local;
+                // K consecutive codes of block k; codes past the window are evaluated
+                // (the table is padded) and discarded
+                const uint32_t c0 = k_clo + K * (j - k_begin);
+#pragma unroll
+                for (int q = 0; q < K; ++q) {
+                    const uint32_t c = c0 + q;
+                    const float2 e = s_bf.sr[c];
+                    float rc[B];
+                    float sse;
+                    if (fast) sse = encode_block<SF, B, 0, false, true>(yb, e.x, e.y, rc);
+                    else sse = encode_block<SF, B, 0, false, false>(yb, e.x, e.y, rc);
+                    const unsigned long long cand = (q == 0 || c < k_chi) ? pack_candidate(sse, c) : ~0ull;
+                    local = cand < local ? cand : local;
+                }
             }
             atomicMin(&W.best[k], local);
         }
