@@ -894,10 +894,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                 // K consecutive codes of block k; codes past the window are evaluated
                 // (the table is padded) and discarded
                 const uint32_t c0 = k_clo + K * (j - k_begin);
+                float2 es[K];
+#pragma unroll
+                for (int q = 0; q < K; ++q) es[q] = s_bf.sr[c0 + q];
 #pragma unroll
                 for (int q = 0; q < K; ++q) {
                     const uint32_t c = c0 + q;
-                    const float2 e = s_bf.sr[c];
+                    const float2 e = es[q];
                     float rc[B];
                     float sse;
                     if (fast) sse = encode_block<SF, B, 0, false, true>(yb, e.x, e.y, rc);
