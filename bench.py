@@ -183,7 +183,7 @@ def build_step(F, S, torch, dev):
     names = ["normal", "laplace", "normal_1e-4", "laplace_1e-4"]
     R, C = host["normal"].shape
     X = {k: S.to_torch(host[k], S.F32, dev) for k in names}
-    keep = []                                    # keep tensors and configs alive
+    keep = list(X.values())                      # keep tensors and configs alive
 
     def t_empty(shape, dtype):
         t = torch.empty(shape, dtype=dtype, device=dev)
@@ -274,7 +274,7 @@ def build_step(F, S, torch, dev):
                            F.F32, C, ptr(grad_c), stream),
                           8 * R * C + 2 * R * C // K + R * C // B + 4 * R * C // K, R * C, "focus_bwd", {}))
     torch.cuda.synchronize()
-    return calls, keep, host
+    return calls, keep, host, X
 
 
 def cpu_baseline(O, S, host, rows_per_tensor):
@@ -329,7 +329,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] generating and uploading the workload", file=sys.stderr, flush=True)
-    calls, keep, host = build_step(F, S, torch, dev)
+    calls, keep, host, X = build_step(F, S, torch, dev)
     step_bytes = sum(c.nbytes for c in calls)
 
     def step(record=False):
@@ -432,6 +432,24 @@ def main():
     roofline["traffic"] = None if traffic is None else round(traffic / 1e6, 2)
     roofline["traffic_unit"] = "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roofline["algorithmic_MB_per_launch"] = round(dom[0][0].nbytes / 1e6, 2)
+    # the practical HBM ceiling of this access pattern: device copies of the same
+    # four 64 MiB inputs, in the same rotation, into four 64 MiB buffers
+    names = list(X)
+    dsts = [torch.empty_like(X[n]) for n in names]
+    copy_ms = []
+    for i in range(32 + 4):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dsts[(i + 1) % 4].copy_(X[names[i % 4]])
+        e1.record()
+        copy_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    cms = float(np.mean([a.elapsed_time(b) for a, b in copy_ms[4:]]))
+    copy_gbs = 2 * X[names[0]].numel() * 4 / (cms * 1e6)
+    del dsts
+    for k, v in breakdown.items():
+        v["frac_of_copy"] = round(v["GB/s"] / copy_gbs, 4)
     stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
     sb = sum(c.nbytes for c, _ in stream_quant)
     sms = sum(ms for _, ms in stream_quant)
@@ -456,8 +474,13 @@ def main():
                    "calls_per_step": len(calls), "algorithmic_bytes_per_step": step_bytes},
         "roofline": roofline,
         "streaming_absmax_4over6": {"GB/s": round(sb / (sms * 1e6), 1),
-                                    "hbm_frac": round(sb / (sms * 1e6) / HBM_PEAK_GBS, 4)},
+                                    "hbm_frac": round(sb / (sms * 1e6) / HBM_PEAK_GBS, 4),
+                                    "frac_of_copy": round(sb / (sms * 1e6) / copy_gbs, 4)},
         "per_strategy": breakdown,
+        "copy_reference": {"GB/s": round(copy_gbs, 1), "hbm_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+                           "what": "device copy (read + write bytes) of the four 64 MiB inputs in rotation, "
+                                   "the same access pattern as the quantize calls; per_strategy frac_of_copy "
+                                   "is GB/s relative to it"},
     }
 
     if not args.no_cpu_baseline:

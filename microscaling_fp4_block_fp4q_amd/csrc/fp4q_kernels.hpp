@@ -219,10 +219,14 @@ __device__ __forceinline__ float encode_block(const float (&y)[U], float S, floa
 }
 
 // encode_block at an E4M3 scale chosen per lane: division-free when S is in
-// range, IEEE division otherwise (zero scales, extreme g).
+// range, IEEE division otherwise (extreme g).  A zero scale with finite
+// elements also takes the division-free path with R = 0, which yields the
+// quotient 0 that a zero scale defines (q0 = 0, residual a, correction 0).
 template <int B, int OFF, bool NAN_GUARD, int U>
 __device__ __forceinline__ float encode_block_e4m3(const float (&y)[U], float S, float (&r)[B]) {
-    if (fast_quotient_range(S)) return encode_block<SF_E4M3, B, OFF, NAN_GUARD, true>(y, S, 1.0f / S, r);
+    const bool zero = !NAN_GUARD && S == 0.0f;
+    if (fast_quotient_range(S) || zero)
+        return encode_block<SF_E4M3, B, OFF, NAN_GUARD, true>(y, S, zero ? 0.0f : 1.0f / S, r);
     return encode_block<SF_E4M3, B, OFF, NAN_GUARD, false>(y, S, 0.0f, r);
 }
 
