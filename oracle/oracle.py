@@ -18,6 +18,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "fp4q_oracle.c")
 LIB = os.path.join(HERE, "liboracle_fp4q.so")
+# A prebuilt oracle library to load instead of building SRC: the mutation
+# test points this at deliberately broken copies of the oracle to show that
+# the pins catch them.
+ALT_LIB = os.environ.get("FP4Q_ORACLE_LIB")
 
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 SF_E8M0, SF_E4M3 = 0, 1
@@ -29,6 +33,8 @@ CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-s
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain C, no intrinsics, no fast-math)."""
+    if ALT_LIB:
+        return ALT_LIB
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp"
         subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"])
@@ -42,8 +48,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(LIB)
+        L = ctypes.CDLL(build())
         f, i, i64, p = ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
         L.oracle_e2m1_mag.argtypes, L.oracle_e2m1_mag.restype = [f], i
         L.oracle_e2m1_value.argtypes, L.oracle_e2m1_value.restype = [i], ctypes.c_double

@@ -135,3 +135,50 @@ def test_deterministic_across_runs(O_lib):
         b = gpu_quantize(x, S.F32, cfg)
         for k in ("codes", "scales", "dequant", "mse"):
             assert_same(a[k], b[k], k)
+
+
+def boundary_tensor(g):
+    """Row c holds, for E4M3 code c (S = fl(dec(c) g)), the elements
+    fl(m S) and its two fp32 neighbours for every E2M1 rounding boundary m
+    (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5), then m = 6 (the largest grid value),
+    with alternating signs; 24 values, padded with zeros to 32."""
+    dec = np.array([O.e4m3_decode(c) for c in range(127)], np.float64)
+    bounds = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    x = np.zeros((127, 32), np.float32)
+    for c in range(1, 127):
+        S = np.float32(np.float32(dec[c]) * np.float32(g))
+        vals = []
+        for m in bounds[:7]:
+            v = np.float32(m * S)
+            vals += [np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))]
+        vals += [np.float32(6 * S), np.nextafter(np.float32(6 * S), np.float32(np.inf)), np.float32(0)]
+        row = np.array(vals, np.float32)
+        row[1::2] *= -1
+        x[c, :24] = row
+    return x
+
+
+@pytest.mark.parametrize("g", [1.0, 0.3, 2.0 ** -20])
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_quotients_on_rounding_boundaries(O_lib, g, B):
+    """Caller-given scales: row c is encoded at code c, so every quotient lies
+    on, or one ulp off, an E2M1 rounding boundary (ties and their neighbours)."""
+    x = boundary_tensor(g)
+    scales = np.repeat(np.arange(127, dtype=np.uint8)[:, None], 32 // B, axis=1)
+    cfg = F.config(E4M3, B, F.GIVEN, F.GLOBAL_USER, g)
+    note(f"rounding-boundary quotients g={g} B={B}")
+    gpu = gpu_quantize(x, S.F32, cfg, scales_in=scales)
+    ref = oracle_quantize(x, S.F32, cfg, scales_in=scales)
+    compare_quant(gpu, ref)
+
+
+@pytest.mark.parametrize("strategy", [F.ABSMAX, F.PREVENT_ZERO, F.FOUR_OVER_SIX, F.BRUTE_FORCE])
+def test_boundary_blocks_every_strategy(O_lib, strategy):
+    """The same boundary rows with the scale chosen by each strategy."""
+    x = boundary_tensor(0.3)
+    cfg = F.config(E4M3, 8, strategy, F.GLOBAL_TENSOR_AMAX)
+    note(f"rounding-boundary blocks strategy={strategy}")
+    gpu = gpu_quantize(x, S.F32, cfg)
+    ref = oracle_quantize(x, S.F32, cfg)
+    assert gpu["g"].view(np.uint32) == ref["g"].view(np.uint32)
+    compare_quant(gpu, ref)
