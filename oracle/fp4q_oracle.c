@@ -53,7 +53,11 @@
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 enum { SF_E8M0 = 0, SF_E4M3 = 1 };
 enum { ST_ABSMAX = 0, ST_PREVENT_ZERO = 1, ST_FOUR_OVER_SIX = 2, ST_BRUTE_FORCE = 3, ST_GIVEN = 4 };
-enum { GM_NONE = 0, GM_TENSOR_AMAX = 1, GM_USER = 2 };
+enum { GM_NONE = 0, GM_TENSOR_AMAX = 1, GM_USER = 2, GM_SEARCH = 3 };
+
+/* Candidate shrink factors of the per-tensor scale search: rho_j = 1 - j/64,
+ * j = 0 .. SEARCH_CANDIDATES - 1 (exact in fp32). */
+#define SEARCH_CANDIDATES 32
 
 #define E4M3_NAN_CODE 0x7F
 #define E8M0_NAN_CODE 0xFF
@@ -401,6 +405,69 @@ float oracle_tensor_global_scale(const void* x, int x_dt, int64_t rows, int64_t 
     return g;
 }
 
+/* fp64 balanced binary tree over v[0:n] zero-padded to len (a power of two
+ * >= n): sum(v[0:len]) = sum(v[0:len/2]) + sum(v[len/2:len]). */
+static double tree_sum_f64_padded(const double* v, int64_t n, int64_t len)
+{
+    if (n <= 0) return 0.0;
+    if (len == 1) return v[0];
+    int64_t half = len / 2;
+    double left = tree_sum_f64_padded(v, n < half ? n : half, half);
+    double right = tree_sum_f64_padded(v + half, n - half, half);
+    return left + right;
+}
+
+/* MSE-optimised per-tensor scale ([MR-GPTQ] section 2.2: scale grids chosen
+ * for minimum MSE per tensor; [FINER] part 2 names optimal scale selection as
+ * open).  Starting from the hierarchical scale g0 of the (rotated) tensor,
+ * candidates g_j = fl(g0 * rho_j) shrink it so that the largest blocks clip
+ * in exchange for finer scales elsewhere; each candidate quantizes every
+ * block with the inner strategy (E4M3 scales) and scores the tensor by the
+ * fp64 tree sum (over all blocks in row-major order, zero-padded to a power
+ * of two) of the fp32 block SSEs.  The smallest total wins, ties to the
+ * smallest j (the least shrink).  totals (optional) receives the
+ * SEARCH_CANDIDATES sums.  A tensor with NaN or infinity gives g = NaN. */
+static float search_global_scale(int strategy, int B, const float* y, int64_t rows, int64_t cols,
+                                 double* totals)
+{
+    float g0 = oracle_global_scale(y, rows * cols);
+    int64_t nblk = rows * (cols / B), len = 1;
+    while (len < nblk) len <<= 1;
+    double* sse = (double*)malloc(sizeof(double) * (size_t)(nblk > 0 ? nblk : 1));
+    if (!sse) return canonical_nan(0);
+    int best = 0;
+    double best_total = 0.0;
+    for (int j = 0; j < SEARCH_CANDIDATES; ++j) {
+        float g = g0 * (float)(1.0 - j / 64.0);
+        for (int64_t b = 0; b < nblk; ++b) {
+            const float* yb = y + b * B;            /* blocks are consecutive in row-major order */
+            int code = choose_scale(SF_E4M3, strategy, yb, B, g, 0);
+            float S = (code == E4M3_NAN_CODE) ? canonical_nan(0) : effective_scale(SF_E4M3, code, g);
+            sse[b] = (double)oracle_block_sse(yb, B, S);
+        }
+        double total = tree_sum_f64_padded(sse, nblk, len);
+        if (totals) totals[j] = total;
+        if (j == 0 || total < best_total || (isnan(best_total) && !isnan(total))) {
+            best = j;
+            best_total = total;
+        }
+    }
+    free(sse);
+    return g0 * (float)(1.0 - best / 64.0);
+}
+
+/* The searched per-tensor scale of x and, optionally, the candidates'
+ * totals; lets tests check the search on its own. */
+float oracle_global_scale_search(int strategy, int B, int H, const void* x, int x_dt, int64_t rows,
+                                 int64_t cols, int64_t ld_x, double* totals)
+{
+    float* y = widen_and_rotate(x, x_dt, rows, cols, ld_x, H);
+    if (!y) return canonical_nan(0);
+    float g = search_global_scale(strategy, B, y, rows, cols, totals);
+    free(y);
+    return g;
+}
+
 /* Quantize a [rows, cols] tensor in blocks of B along each row.
  * Outputs (each may be NULL): packed codes [rows, cols/2] (low nibble = even
  * column), scales [rows, cols/B] (input when strategy is GIVEN), g_out,
@@ -415,7 +482,7 @@ int oracle_quantize(int fmt, int B, int strategy, int global_mode, float user_g,
     if (H != 0 && H != 16 && H != 32) return -1;
     if (cols % B || (H && cols % H) || cols % 2) return -1;
     if (fmt == SF_E8M0 && (global_mode != GM_NONE || strategy == ST_FOUR_OVER_SIX)) return -1;
-    if (strategy == ST_GIVEN && !scales) return -1;
+    if (strategy == ST_GIVEN && (!scales || global_mode == GM_SEARCH)) return -1;
 
     float* y = widen_and_rotate(x, x_dt, rows, cols, ld_x, H);
     if (!y) return -1;
@@ -423,6 +490,7 @@ int oracle_quantize(int fmt, int B, int strategy, int global_mode, float user_g,
     float g = 1.0f;
     if (global_mode == GM_USER) g = user_g;
     else if (global_mode == GM_TENSOR_AMAX) g = oracle_global_scale(y, rows * cols);
+    else if (global_mode == GM_SEARCH) g = search_global_scale(strategy, B, y, rows, cols, NULL);
     if (g_out) *g_out = g;
 
     int64_t nb = cols / B;

@@ -26,7 +26,8 @@ ALT_LIB = os.environ.get("FP4Q_ORACLE_LIB")
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 SF_E8M0, SF_E4M3 = 0, 1
 ABSMAX, PREVENT_ZERO, FOUR_OVER_SIX, BRUTE_FORCE, GIVEN = 0, 1, 2, 3, 4
-GLOBAL_NONE, GLOBAL_TENSOR_AMAX, GLOBAL_USER = 0, 1, 2
+GLOBAL_NONE, GLOBAL_TENSOR_AMAX, GLOBAL_USER, GLOBAL_SEARCH = 0, 1, 2, 3
+SEARCH_CANDIDATES = 32
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
@@ -67,6 +68,8 @@ def lib():
         L.oracle_global_scale.argtypes, L.oracle_global_scale.restype = [p, i64], f
         L.oracle_tensor_global_scale.argtypes = [p, i, i64, i64, i64, i]
         L.oracle_tensor_global_scale.restype = f
+        L.oracle_global_scale_search.argtypes = [i, i, i, p, i, i64, i64, i64, p]
+        L.oracle_global_scale_search.restype = f
         L.oracle_quantize.argtypes = [i, i, i, i, f, i, p, i, i64, i64, i64,
                                       p, p, p, p, i, i64, p, p]
         L.oracle_quantize.restype = i
@@ -181,6 +184,18 @@ def tensor_global_scale(x: np.ndarray, *, hadamard: int = 0, x_dt: int | None = 
 # --------------------------------------------------------------------------
 # tensor entry points
 # --------------------------------------------------------------------------
+
+def global_scale_search(x: np.ndarray, *, block: int, strategy: int = ABSMAX, hadamard: int = 0,
+                        x_dt: int | None = None):
+    """The MSE-searched per-tensor scale of x (E4M3 block scales) and the
+    fp64 total SSE of each of the SEARCH_CANDIDATES candidates."""
+    rows, cols = x.shape
+    xd = _dt_of(x, x_dt)
+    x = np.ascontiguousarray(x)
+    totals = np.zeros(SEARCH_CANDIDATES, np.float64)
+    g = lib().oracle_global_scale_search(strategy, block, hadamard, _ptr(x), xd, rows, cols, cols, _ptr(totals))
+    return np.float32(g), totals
+
 
 def quantize(x: np.ndarray, *, fmt: int, block: int, strategy: int = ABSMAX,
              global_mode: int = GLOBAL_NONE, user_g: float = 1.0, hadamard: int = 0,
