@@ -59,12 +59,13 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 1
+#define FP4Q_ABI_VERSION 2
 
 typedef enum {
     FP4Q_OK = 0,
     FP4Q_ERR_INVALID_ARG = 1, /* null required pointer, bad enum, bad user scale */
-    FP4Q_ERR_UNSUPPORTED = 2, /* combination the formats do not define */
+    FP4Q_ERR_UNSUPPORTED = 2, /* combination the formats do not define, or SEARCH
+                                 with BRUTE_FORCE or GIVEN */
     FP4Q_ERR_SHAPE = 3,       /* block / rotation / sub-block does not tile the row */
     FP4Q_ERR_ALIGNMENT = 4,   /* base pointer or row pitch not 16-byte aligned */
     FP4Q_ERR_DEVICE = 5       /* the HIP runtime refused a launch */
@@ -93,11 +94,18 @@ typedef enum {
 /* Per-tensor scale g (hierarchical scaling, same page, method part 2):
  * NONE -> g = 1; TENSOR_AMAX -> g = fl(amax(|x|) / 2688) over the whole
  * (rotated) tensor, 2688 = 6 * 448, and g = 1 when that is 0, NaN when the
- * tensor holds NaN or infinity; USER -> g = global_scale.  E4M3 only. */
+ * tensor holds NaN or infinity; USER -> g = global_scale.  E4M3 only.
+ * SEARCH (per-tensor scale chosen for minimum MSE, MR-GPTQ page, section
+ * 2.2): with g0 the TENSOR_AMAX scale, the candidates g_j = fl(g0 (1 - j/64)),
+ * j = 0..31, are each scored by the fp64 balanced-tree sum, over all blocks
+ * in row-major order (zero-padded to a power of two), of the fp32 block SSE
+ * under the configured strategy; the smallest total wins, ties to the
+ * smallest j.  Strategies ABSMAX, PREVENT_ZERO and FOUR_OVER_SIX. */
 typedef enum {
     FP4Q_GLOBAL_NONE = 0,
     FP4Q_GLOBAL_TENSOR_AMAX = 1,
-    FP4Q_GLOBAL_USER = 2
+    FP4Q_GLOBAL_USER = 2,
+    FP4Q_GLOBAL_SEARCH = 3
 } fp4q_global;
 
 typedef struct {
@@ -118,8 +126,9 @@ const char* fp4q_status_string(int status);
 
 /* Bytes of caller-provided device workspace `fp4q_quantize` and
  * `fp4q_scale_search` need for this configuration and shape (0 when none):
- * room for the per-tensor abs-max partial results of TENSOR_AMAX.  Returns
- * 0 for a NULL config. */
+ * room for the per-tensor abs-max partial results of TENSOR_AMAX, and for
+ * SEARCH also the candidates' partial sums (about 32 * 8 bytes per 64 * 4
+ * elements).  Returns 0 for a NULL config. */
 size_t fp4q_workspace_bytes(const fp4q_config* cfg, int64_t rows, int64_t cols);
 
 /* Quantize x [rows, cols] (type x_dt, row stride ld_x) into packed E2M1
@@ -127,8 +136,9 @@ size_t fp4q_workspace_bytes(const fp4q_config* cfg, int64_t rows, int64_t cols);
  *   codes      [rows, cols/2]      required output
  *   scales     [rows, cols/block]  required; output, or input for GIVEN
  *   g_dev      1 fp32              output of the g used; required for
- *                                  TENSOR_AMAX and USER, optional for NONE
- *                                  (then 1.0 is written when non-NULL)
+ *                                  TENSOR_AMAX, USER and SEARCH, optional
+ *                                  for NONE (then 1.0 is written when
+ *                                  non-NULL)
  *   dequant    [rows, ld_dq]       optional output (type dq_dt): the fp32
  *                                  dequantized value (-1)^s fl(grid * S),
  *                                  rounded half-to-even to bf16 / fp16

@@ -29,12 +29,15 @@ fp4q_status check_config(const fp4q_config* cfg) {
     if (!cfg || cfg->struct_size != sizeof(fp4q_config)) return FP4Q_ERR_INVALID_ARG;
     if (cfg->scale_fmt != FP4Q_SCALE_E8M0 && cfg->scale_fmt != FP4Q_SCALE_E4M3) return FP4Q_ERR_INVALID_ARG;
     if (cfg->strategy < FP4Q_ABSMAX || cfg->strategy > FP4Q_GIVEN) return FP4Q_ERR_INVALID_ARG;
-    if (cfg->global_mode < FP4Q_GLOBAL_NONE || cfg->global_mode > FP4Q_GLOBAL_USER) return FP4Q_ERR_INVALID_ARG;
+    if (cfg->global_mode < FP4Q_GLOBAL_NONE || cfg->global_mode > FP4Q_GLOBAL_SEARCH) return FP4Q_ERR_INVALID_ARG;
     if (cfg->hadamard < 0) return FP4Q_ERR_INVALID_ARG;
     if (cfg->block != 4 && cfg->block != 8 && cfg->block != 16 && cfg->block != 32) return FP4Q_ERR_SHAPE;
     if (cfg->hadamard != 0 && cfg->hadamard != 16 && cfg->hadamard != 32) return FP4Q_ERR_UNSUPPORTED;
     if (cfg->scale_fmt == FP4Q_SCALE_E8M0 &&
         (cfg->global_mode != FP4Q_GLOBAL_NONE || cfg->strategy == FP4Q_FOUR_OVER_SIX))
+        return FP4Q_ERR_UNSUPPORTED;
+    if (cfg->global_mode == FP4Q_GLOBAL_SEARCH &&
+        (cfg->strategy == FP4Q_BRUTE_FORCE || cfg->strategy == FP4Q_GIVEN))
         return FP4Q_ERR_UNSUPPORTED;
     if (cfg->global_mode == FP4Q_GLOBAL_USER) {
         const double g = cfg->global_scale;
@@ -76,6 +79,17 @@ int unit_of(int x_dt, int block, int H) {
     return u;
 }
 
+// Workspace of the per-tensor scale search: abs-max partials, then the
+// candidates' per-tile sums, then one reduction level's sums.
+constexpr size_t kAmaxBytes = (size_t)kAmaxBlocks * sizeof(uint32_t);
+
+int64_t search_tiles(int64_t rows, int64_t cols, int U) { return (rows * cols / U + kTileUnits - 1) / kTileUnits; }
+
+size_t search_workspace_bytes(int64_t tiles) {
+    const int64_t level = (tiles + 2 * kThreads - 1) / (2 * kThreads);
+    return kAmaxBytes + (size_t)kSearchCandidates * sizeof(double) * (size_t)(tiles + level);
+}
+
 #define FP4Q_TRY(expr)                           \
     do {                                         \
         fp4q_status st_ = (expr);                \
@@ -106,7 +120,8 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
     if (dequant) FP4Q_TRY(check_tensor(dequant, dq_dt, rows, cols, ld_dq));
     if (mse) FP4Q_TRY(check_buffer(mse));
     if (sse) FP4Q_TRY(check_buffer(sse));
-    const bool tamax = cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX;
+    const bool search = cfg->global_mode == FP4Q_GLOBAL_SEARCH;
+    const bool tamax = cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX || search;
     if (tamax) FP4Q_TRY(check_buffer(workspace));
 
     if (tamax) {
@@ -122,6 +137,43 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
     }
 
     const int U = unit_of(x_dt, B, H);
+    if (search) {
+        GSearchArgs ga{};
+        ga.x = x;
+        ga.ld_x = ld_x;
+        ga.units = rows * cols / U;
+        ga.units_per_row = cols / U;
+        ga.contiguous = ld_x == cols;
+        ga.amax_partials = reinterpret_cast<const uint32_t*>(workspace);
+        ga.n_partials = kAmaxBlocks;
+        ga.prevent_zero = cfg->strategy == FP4Q_PREVENT_ZERO;
+        ga.ntiles = search_tiles(rows, cols, U);
+        double* level0 = reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) + kAmaxBytes);
+        double* level1 = level0 + (size_t)kSearchCandidates * ga.ntiles;
+        ga.partials = level0;
+        const int st = cfg->strategy == FP4Q_FOUR_OVER_SIX ? ST_FOUR_OVER_SIX : ST_ABSMAX;
+        const int grid = grid_for(ga.units);
+        hipError_t e;
+        switch (x_dt) {
+        case FP4Q_F32: e = launch_gsearch_f32(ga, B, H, st, grid, s); break;
+        case FP4Q_BF16: e = launch_gsearch_bf16(ga, B, H, st, grid, s); break;
+        default: e = launch_gsearch_f16(ga, B, H, st, grid, s); break;
+        }
+        FP4Q_TRY(device_status(e));
+        // tiles -> groups of 512 -> ... -> one total per candidate, alternating buffers
+        const double* src = level0;
+        int64_t n = ga.ntiles, stride = ga.ntiles;
+        while (n > 1) {
+            const int64_t m = (n + 2 * kThreads - 1) / (2 * kThreads);
+            double* dst = src == level0 ? level1 : level0;
+            FP4Q_TRY(device_status(launch_tree_reduce_f64(src, n, stride, dst, m, s)));
+            src = dst;
+            n = m;
+            stride = m;
+        }
+        FP4Q_TRY(device_status(launch_gsearch_pick(src, stride, ga.amax_partials, kAmaxBlocks, g_dev, s)));
+    }
+
     QuantArgs qa{};
     qa.x = x;
     qa.ld_x = ld_x;
@@ -139,8 +191,10 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
     qa.sse = sse;
     qa.amax_partials = reinterpret_cast<const uint32_t*>(workspace);
     qa.n_partials = tamax ? kAmaxBlocks : 0;
-    qa.global_mode = cfg->global_mode;
+    qa.global_mode = search ? GM_DEVICE : cfg->global_mode;
     qa.user_g = cfg->global_scale;
+    qa.g_in = g_dev;
+    if (search) qa.g_out = nullptr;      // g_dev already holds the searched scale
     qa.prevent_zero = cfg->strategy == FP4Q_PREVENT_ZERO;
     const int grid = grid_for(qa.units);
     hipError_t e;
@@ -178,10 +232,13 @@ const char* fp4q_status_string(int status) {
 }
 
 size_t fp4q_workspace_bytes(const fp4q_config* cfg, int64_t rows, int64_t cols) {
-    (void)rows;
-    (void)cols;
     if (!cfg) return 0;
-    return cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX ? (size_t)kAmaxBlocks * sizeof(uint32_t) : 0;
+    if (cfg->global_mode == FP4Q_GLOBAL_SEARCH) {
+        // the most units any input type gives: fp32, U = max(4, block, hadamard)
+        const int U = unit_of(FP4Q_F32, cfg->block > 0 ? cfg->block : 1, cfg->hadamard > 0 ? cfg->hadamard : 0);
+        return search_workspace_bytes(rows > 0 && cols > 0 ? search_tiles(rows, cols, U) : 0);
+    }
+    return cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX ? kAmaxBytes : 0;
 }
 
 fp4q_status fp4q_quantize(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,

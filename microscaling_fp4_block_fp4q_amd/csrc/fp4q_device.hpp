@@ -21,7 +21,9 @@ namespace fp4q_dev {
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 enum : int { SF_E8M0 = 0, SF_E4M3 = 1 };
 enum : int { ST_ABSMAX = 0, ST_PREVENT_ZERO = 1, ST_FOUR_OVER_SIX = 2, ST_BRUTE_FORCE = 3, ST_GIVEN = 4 };
-enum : int { GM_NONE = 0, GM_TENSOR_AMAX = 1, GM_USER = 2 };
+// Per-tensor scale modes of the kernels; GM_DEVICE reads g from device
+// memory (the searched scale).
+enum : int { GM_NONE = 0, GM_TENSOR_AMAX = 1, GM_USER = 2, GM_DEVICE = 3 };
 
 constexpr uint32_t kQNaN = 0x7FC00000u;
 constexpr uint32_t kE4M3NaN = 0x7Fu;
@@ -271,13 +273,13 @@ __device__ __forceinline__ void load_codes(const uint8_t* __restrict__ p, uint32
 // ---------------------------------------------------------------------------
 
 // Balanced binary tree sum in index order over v[OFF, OFF+N).
-template <int N, int OFF = 0, int M>
-__device__ __forceinline__ float tree_sum(const float (&v)[M]) {
+template <int N, int OFF = 0, class T, int M>
+__device__ __forceinline__ T tree_sum(const T (&v)[M]) {
     if constexpr (N == 1) {
         return v[OFF];
     } else {
-        float l = tree_sum<N / 2, OFF>(v);
-        float r = tree_sum<N / 2, OFF + N / 2>(v);
+        T l = tree_sum<N / 2, OFF>(v);
+        T r = tree_sum<N / 2, OFF + N / 2>(v);
         return l + r;
     }
 }

@@ -18,6 +18,7 @@ namespace fp4q_dev {
 
 constexpr int kThreads = 256;
 constexpr int kAmaxBlocks = 1024;   // partial abs-max results of the pre-pass
+constexpr int kSearchCandidates = 32;   // per-tensor scale candidates g0 * (1 - j/64)
 
 template <int... Is> struct ISeq {};
 template <int N, int... Is> struct MakeISeq : MakeISeq<N - 1, N - 1, Is...> {};
@@ -56,7 +57,22 @@ struct QuantArgs {
     int n_partials;
     int global_mode;
     float user_g;
+    const float* g_in;      // GM_DEVICE: the scale to use
     int prevent_zero;
+};
+
+// Per-tensor scale search: block SSE totals of every candidate, per tile.
+struct GSearchArgs {
+    const void* x;
+    int64_t ld_x;
+    int64_t units;
+    int64_t units_per_row;
+    int contiguous;
+    const uint32_t* amax_partials;
+    int n_partials;
+    int prevent_zero;
+    double* partials;       // [kSearchCandidates][ntiles]
+    int64_t ntiles;
 };
 
 struct AmaxArgs {
@@ -151,16 +167,24 @@ __device__ __forceinline__ float canonical_nan_like(float s) { return as_f(kQNaN
 // Right Scaling)", method part 2): NONE -> 1, USER -> given, TENSOR_AMAX ->
 // fl(amax / (6 * 448)), 1 when that is 0, NaN when amax is not finite.
 // Every thread of the workgroup must call it.
-__device__ __forceinline__ float workgroup_global_scale(const QuantArgs& p) {
-    if (p.global_mode == GM_NONE) return 1.0f;
-    if (p.global_mode == GM_USER) return p.user_g;
+__device__ __forceinline__ float workgroup_amax_scale(const uint32_t* partials, int n) {
     uint32_t m = 0;
-    for (int i = threadIdx.x; i < p.n_partials; i += kThreads) m = max(m, p.amax_partials[i]);
+    for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, partials[i]);
     m = workgroup_max_u32(m);
     if (m >= 0x7F800000u) return as_f(kQNaN);
     float g = as_f(m) / 2688.0f;
     return g == 0.0f ? 1.0f : g;
 }
+
+__device__ __forceinline__ float workgroup_global_scale(const QuantArgs& p) {
+    if (p.global_mode == GM_NONE) return 1.0f;
+    if (p.global_mode == GM_USER) return p.user_g;
+    if (p.global_mode == GM_DEVICE) return *p.g_in;
+    return workgroup_amax_scale(p.amax_partials, p.n_partials);
+}
+
+// Shrink factor of search candidate j: 1 - j/64 (exact in fp32).
+__device__ __forceinline__ float search_factor(int j) { return 1.0f - (float)j * 0.015625f; }
 
 __device__ __forceinline__ float read_g(const float* g_dev) { return g_dev ? *g_dev : 1.0f; }
 
@@ -694,6 +718,90 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs p) {
             quant_block<SF, ST, B, b>(y, g, six_g, four_g, p.prevent_zero, given[b], cw, sink, sc[b], sse[b]);
         });
         store_unit_outputs<B, U>(p, u0, nvalid, lane, lds, cw, sc, sse, ST != ST_GIVEN);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor scale search (MR-GPTQ page, section 2.2: scales chosen per
+// tensor for minimum MSE).  Candidate g_j = fl(g0 (1 - j/64)); its score is
+// the fp64 balanced tree over all blocks (row-major, zero-padded to a power
+// of two) of the fp32 block SSE the strategy reaches at g_j.  A tile's 64 x NB
+// blocks are an aligned subtree: each lane sums its NB blocks as a tree, the
+// wave combines lanes with an xor butterfly (pairs of neighbours first, so the
+// same tree), and lane 0 stores the tile's subtree sum; k_tree_reduce_f64
+// then combines tiles 512 at a time, again as aligned subtrees.
+// ---------------------------------------------------------------------------
+
+// fp32 SSE of block BI at scale factor g under abs-max (prevent-zero) or
+// 4-over-6, as quant_block chooses and scores it; NaN for a NaN block.
+template <int ST, int B, int BI, int U>
+__device__ __forceinline__ float block_score(const float (&y)[U], uint32_t ab, float g, float six_g, float four_g,
+                                             int prevent_zero) {
+    constexpr int OFF = BI * B;
+    if (ab >= 0x7F800000u || !(g < __builtin_inff())) return as_f(kQNaN);
+    const float a_b = as_f(ab);
+    const uint32_t s6 = e4m3_encode(a_b / six_g);
+    float r[B];
+    if constexpr (ST == ST_ABSMAX) {
+        const uint32_t sc = (prevent_zero && s6 == 0u) ? 1u : s6;
+        return encode_block_e4m3<B, OFF, false>(y, e4m3_value(sc) * g, r);
+    } else {
+        static_assert(ST == ST_FOUR_OVER_SIX, "abs-max, prevent-zero or 4-over-6");
+        const uint32_t s4 = e4m3_encode(a_b / four_g);
+        const float e6 = encode_block_e4m3<B, OFF, false>(y, e4m3_value(s6) * g, r);
+        const float e4 = encode_block_e4m3<B, OFF, false>(y, e4m3_value(s4) * g, r);
+        return e4 < e6 ? e4 : e6;
+    }
+}
+
+template <class InT, int B, int H, int ST>
+__global__ __launch_bounds__(kThreads) void k_gsearch(GSearchArgs p) {
+    constexpr int U = unit_elems<InT, B, H>();
+    constexpr int NB = U / B;
+    __shared__ __attribute__((aligned(16))) char s_tiles[kThreads / 64][kTileUnits * slot_bytes<U>()];
+    const InT* x = reinterpret_cast<const InT*>(p.x);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    char* lds = s_tiles[wave];
+    const float g0 = workgroup_amax_scale(p.amax_partials, p.n_partials);
+
+    const int64_t ntiles = (p.units + kTileUnits - 1) / kTileUnits;
+    const int64_t tstride = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < ntiles; t += tstride) {
+        const int64_t u0 = t * kTileUnits;
+        const int nvalid = (int)min<int64_t>(kTileUnits, p.units - u0);
+        const int64_t u = u0 + lane;
+        const bool active = lane < nvalid;
+        float y[U];
+        if (p.contiguous) {
+            tile_load<InT, U>(x + u0 * U, nvalid, lds, lane, y);
+        } else if (active) {
+            load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, false), y);
+        } else {
+#pragma unroll
+            for (int i = 0; i < U; ++i) y[i] = 0.0f;
+        }
+        if constexpr (H > 0) fwht_segments<H, U>(y);
+        uint32_t ab[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            ab[b] = 0;
+#pragma unroll
+            for (int i = 0; i < B; ++i) ab[b] = max(ab[b], as_u(y[b * B + i]) & 0x7FFFFFFFu);
+        }
+#pragma unroll 1
+        for (int j = 0; j < kSearchCandidates; ++j) {
+            const float g = g0 * search_factor(j);
+            const float six_g = 6.0f * g, four_g = 4.0f * g;
+            double e[NB];
+            static_for<NB>([&](auto bi) {
+                constexpr int b = decltype(bi)::value;
+                e[b] = (double)block_score<ST, B, b>(y, ab[b], g, six_g, four_g, p.prevent_zero);
+            });
+            double s = active ? tree_sum<NB>(e) : 0.0;      // lanes past the tensor are padding
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o, 64);
+            if (lane == 0) p.partials[j * p.ntiles + t] = s;
+        }
     }
 }
 

@@ -13,6 +13,16 @@ hipError_t launch_quant_f32(const QuantArgs& a, int B, int H, int sf, int st, in
 hipError_t launch_quant_bf16(const QuantArgs& a, int B, int H, int sf, int st, int grid, hipStream_t s);
 hipError_t launch_quant_f16(const QuantArgs& a, int B, int H, int sf, int st, int grid, hipStream_t s);
 
+// Per-tensor scale search for one input dtype; st is ST_ABSMAX (with
+// a.prevent_zero) or ST_FOUR_OVER_SIX.
+hipError_t launch_gsearch_f32(const GSearchArgs& a, int B, int H, int st, int grid, hipStream_t s);
+hipError_t launch_gsearch_bf16(const GSearchArgs& a, int B, int H, int st, int grid, hipStream_t s);
+hipError_t launch_gsearch_f16(const GSearchArgs& a, int B, int H, int st, int grid, hipStream_t s);
+hipError_t launch_tree_reduce_f64(const double* in, int64_t n, int64_t in_stride, double* out, int64_t out_stride,
+                                  hipStream_t s);
+hipError_t launch_gsearch_pick(const double* totals, int64_t stride, const uint32_t* amax_partials, int n_partials,
+                               float* g_dev, hipStream_t s);
+
 hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t s);
 hipError_t launch_write_g(float* g_dev, float g, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int B, int DU, int grid, hipStream_t s);
@@ -93,6 +103,33 @@ hipError_t dispatch_quant(const QuantArgs& a, int B, int H, int sf, int st, int 
     case 8: return dispatch_quant_h<InT, 8>(a, H, sf, st, grid, s);
     case 16: return dispatch_quant_h<InT, 16>(a, H, sf, st, grid, s);
     case 32: return dispatch_quant_h<InT, 32>(a, H, sf, st, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class InT, int B, int H>
+hipError_t dispatch_gsearch_st(const GSearchArgs& a, int st, int grid, hipStream_t s) {
+    if (st == ST_FOUR_OVER_SIX) return launch_resident<k_gsearch<InT, B, H, ST_FOUR_OVER_SIX>>(a, grid, s);
+    return launch_resident<k_gsearch<InT, B, H, ST_ABSMAX>>(a, grid, s);
+}
+
+template <class InT, int B>
+hipError_t dispatch_gsearch_h(const GSearchArgs& a, int H, int st, int grid, hipStream_t s) {
+    switch (H) {
+    case 0: return dispatch_gsearch_st<InT, B, 0>(a, st, grid, s);
+    case 16: return dispatch_gsearch_st<InT, B, 16>(a, st, grid, s);
+    case 32: return dispatch_gsearch_st<InT, B, 32>(a, st, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class InT>
+hipError_t dispatch_gsearch(const GSearchArgs& a, int B, int H, int st, int grid, hipStream_t s) {
+    switch (B) {
+    case 4: return dispatch_gsearch_h<InT, 4>(a, H, st, grid, s);
+    case 8: return dispatch_gsearch_h<InT, 8>(a, H, st, grid, s);
+    case 16: return dispatch_gsearch_h<InT, 16>(a, H, st, grid, s);
+    case 32: return dispatch_gsearch_h<InT, 32>(a, H, st, grid, s);
     }
     return hipErrorInvalidValue;
 }

@@ -1,5 +1,6 @@
 // misc_kernels.hip -- launchers of the per-tensor abs-max pre-pass,
-// dequantize, block MSE and FOCUS relaxed forward / backward kernels.
+// dequantize, block MSE and FOCUS relaxed forward / backward kernels; the
+// reduction and pick steps of the per-tensor scale search.
 #include "fp4q_launch.hpp"
 
 namespace fp4q_dev {
@@ -10,6 +11,63 @@ __global__ void k_write_g(float* g_dev, float g) {
 
 hipError_t launch_write_g(float* g_dev, float g, hipStream_t s) {
     hipLaunchKernelGGL(k_write_g, dim3(1), dim3(64), 0, s, g_dev, g);
+    return hipGetLastError();
+}
+
+// One level of the candidates' fp64 trees: out[j][k] = tree of
+// in[j][512 k .. 512 k + 511], entries at or past n counting as 0.
+// Grid (ceil(n / 512), kSearchCandidates).
+__global__ __launch_bounds__(kThreads) void k_tree_reduce_f64(const double* in, int64_t n, int64_t in_stride,
+                                                              double* out, int64_t out_stride) {
+    __shared__ double s[kThreads];
+    const double* src = in + (int64_t)blockIdx.y * in_stride;
+    const int64_t i0 = (int64_t)blockIdx.x * (2 * kThreads) + 2 * threadIdx.x;
+    const double a = i0 < n ? src[i0] : 0.0;
+    const double b = i0 + 1 < n ? src[i0 + 1] : 0.0;
+    s[threadIdx.x] = a + b;
+    __syncthreads();
+    for (int w = kThreads / 2; w >= 1; w >>= 1) {
+        double v = 0.0;
+        if ((int)threadIdx.x < w) v = s[2 * threadIdx.x] + s[2 * threadIdx.x + 1];
+        __syncthreads();
+        if ((int)threadIdx.x < w) s[threadIdx.x] = v;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[(int64_t)blockIdx.y * out_stride + blockIdx.x] = s[0];
+}
+
+// The winning candidate: smallest total (a NaN total never wins over a
+// number), ties to the smallest j; writes g = fl(g0 (1 - j/64)).
+__global__ __launch_bounds__(kThreads) void k_gsearch_pick(const double* totals, int64_t stride,
+                                                           const uint32_t* amax_partials, int n_partials,
+                                                           float* g_dev) {
+    const float g0 = workgroup_amax_scale(amax_partials, n_partials);
+    if (threadIdx.x == 0) {
+        int best = 0;
+        double bt = totals[0];
+        for (int j = 1; j < kSearchCandidates; ++j) {
+            const double t = totals[j * stride];
+            if (t < bt || (bt != bt && t == t)) {
+                best = j;
+                bt = t;
+            }
+        }
+        *g_dev = g0 * search_factor(best);
+    }
+}
+
+hipError_t launch_tree_reduce_f64(const double* in, int64_t n, int64_t in_stride, double* out, int64_t out_stride,
+                                  hipStream_t s) {
+    const int64_t groups = (n + 2 * kThreads - 1) / (2 * kThreads);
+    hipLaunchKernelGGL(k_tree_reduce_f64, dim3((unsigned)groups, kSearchCandidates), dim3(kThreads), 0, s, in, n,
+                       in_stride, out, out_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_gsearch_pick(const double* totals, int64_t stride, const uint32_t* amax_partials, int n_partials,
+                               float* g_dev, hipStream_t s) {
+    hipLaunchKernelGGL(k_gsearch_pick, dim3(1), dim3(kThreads), 0, s, totals, stride, amax_partials, n_partials,
+                       g_dev);
     return hipGetLastError();
 }
 

@@ -8,4 +8,8 @@ hipError_t launch_quant_bf16(const QuantArgs& a, int B, int H, int sf, int st, i
     return dispatch_quant<bf16_t>(a, B, H, sf, st, grid, s);
 }
 
+hipError_t launch_gsearch_bf16(const GSearchArgs& a, int B, int H, int st, int grid, hipStream_t s) {
+    return dispatch_gsearch<bf16_t>(a, B, H, st, grid, s);
+}
+
 }  // namespace fp4q_dev

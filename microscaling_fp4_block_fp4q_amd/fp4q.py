@@ -25,7 +25,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE = ran
 F32, BF16, F16 = 0, 1, 2
 E8M0, E4M3 = 0, 1
 ABSMAX, PREVENT_ZERO, FOUR_OVER_SIX, BRUTE_FORCE, GIVEN = range(5)
-GLOBAL_NONE, GLOBAL_TENSOR_AMAX, GLOBAL_USER = range(3)
+GLOBAL_NONE, GLOBAL_TENSOR_AMAX, GLOBAL_USER, GLOBAL_SEARCH = range(4)
 
 
 class Config(ctypes.Structure):

@@ -36,12 +36,18 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_version_strings_workspace():
-    assert F.abi_version() == 1
+    assert F.abi_version() == 2
     for s in range(6):
         assert F.status_string(s) and F.status_string(s) != "unknown status"
     assert F.status_string(99) == "unknown status"
     assert F.workspace_bytes(F.nvfp4(), 4096, 4096) >= 4
     assert F.workspace_bytes(F.mxfp4(), 4096, 4096) == 0
+    # search: abs-max partials + 32 fp64 sums per tile of 64 units (fp32: 4 elements per unit at
+    # block 4) + one reduction level
+    tiles = 4096 * 4096 // 4 // 64
+    want = 4096 + 32 * 8 * (tiles + (tiles + 511) // 512)
+    assert F.workspace_bytes(F.config(F.E4M3, 4, F.ABSMAX, F.GLOBAL_SEARCH), 4096, 4096) == want
+    assert F.workspace_bytes(F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_SEARCH), 0, 64) == 4096
     assert F.lib().fp4q_workspace_bytes(None, 1, 1) == 0
 
 
@@ -68,6 +74,11 @@ def test_quantize_validation():
     assert quant(F.config(1, 16, hadamard=8)) == F.ERR_UNSUPPORTED
     assert quant(F.config(0, 32, 0, F.GLOBAL_TENSOR_AMAX)) == F.ERR_UNSUPPORTED  # E8M0 + g
     assert quant(F.config(0, 32, F.FOUR_OVER_SIX)) == F.ERR_UNSUPPORTED          # E8M0 + 4/6
+    assert quant(F.config(0, 32, 0, F.GLOBAL_SEARCH)) == F.ERR_UNSUPPORTED       # E8M0 + search
+    assert quant(F.config(1, 16, F.BRUTE_FORCE, F.GLOBAL_SEARCH)) == F.ERR_UNSUPPORTED
+    assert quant(F.config(1, 16, F.GIVEN, F.GLOBAL_SEARCH)) == F.ERR_UNSUPPORTED
+    assert quant(F.config(1, 16, 0, F.GLOBAL_SEARCH), g=0) == F.ERR_INVALID_ARG  # writes g
+    assert quant(F.config(1, 16, 0, F.GLOBAL_SEARCH), ws=0) == F.ERR_INVALID_ARG # needs workspace
     for gs in (0.0, -1.0, float("inf"), float("nan"), 1e-39, 1e36):
         assert quant(F.config(1, 16, 0, F.GLOBAL_USER, gs)) == F.ERR_INVALID_ARG, gs
     assert quant(nv, x=0) == F.ERR_INVALID_ARG
