@@ -43,7 +43,10 @@
  * Parity pins: every function here is checked by tests/test_oracle_*.py
  * against something other than itself (exact rational arithmetic, torch's
  * float8/bfloat16/float16 casts, scipy's Hadamard matrix, closed forms,
- * brute force, finite differences).  None is "parity unpinned".
+ * brute force, finite differences).  One reading has nothing to pin it:
+ * the exponent bias 15 of the UE5M3 scale format, which no page states
+ * ("parity unpinned" for that bias; its rounding, saturation and use in
+ * every strategy are pinned like E4M3's).
  */
 #include <math.h>
 #include <stdint.h>
@@ -51,7 +54,7 @@
 #include <string.h>
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
-enum { SF_E8M0 = 0, SF_E4M3 = 1 };
+enum { SF_E8M0 = 0, SF_E4M3 = 1, SF_UE5M3 = 2 };
 enum { ST_ABSMAX = 0, ST_PREVENT_ZERO = 1, ST_FOUR_OVER_SIX = 2, ST_BRUTE_FORCE = 3, ST_GIVEN = 4 };
 enum { GM_NONE = 0, GM_TENSOR_AMAX = 1, GM_USER = 2, GM_SEARCH = 3 };
 
@@ -60,6 +63,7 @@ enum { GM_NONE = 0, GM_TENSOR_AMAX = 1, GM_USER = 2, GM_SEARCH = 3 };
 #define SEARCH_CANDIDATES 32
 
 #define E4M3_NAN_CODE 0x7F
+#define UE5M3_NAN_CODE 0xFF
 #define E8M0_NAN_CODE 0xFF
 #define QNAN_BITS 0x7FC00000u
 
@@ -128,6 +132,39 @@ double oracle_e8m0_decode(int code)
     code &= 0xFF;
     if (code == E8M0_NAN_CODE) return NAN;
     return ldexp(1.0, code - 127);
+}
+
+/* UE5M3: the unsigned wide-exponent scale format the Finer-is-Better page
+ * (key findings and significance) sets against E4M3 + hierarchical scaling
+ * + 4-over-6.  The page gives no encoding; reading: 5 exponent bits with
+ * bias 15, 3 mantissa bits, subnormals m * 2^-17, no infinities, 0xFF NaN,
+ * so the largest value is 0xFE = 1.75 * 2^16.  (The bias is a reading with
+ * nothing on the page to pin it: parity unpinned for the bias.) */
+double oracle_ue5m3_decode(int code)
+{
+    code &= 0xFF;
+    if (code == UE5M3_NAN_CODE) return NAN;
+    int e = code >> 3, m = code & 7;
+    if (e == 0) return m * ldexp(1.0, -17);
+    return (1.0 + m / 8.0) * ldexp(1.0, e - 15);
+}
+
+/* Round v >= 0 to the nearest finite UE5M3 value, ties to the even code,
+ * saturating at the largest value; NaN -> the NaN code.  Plain search over
+ * the 255 finite codes. */
+int oracle_ue5m3_encode(float v)
+{
+    if (isnan(v)) return UE5M3_NAN_CODE;
+    double a = fabs((double)v);
+    double top = oracle_ue5m3_decode(0xFE);
+    if (a >= top) return 0xFE;
+    int best = 0;
+    double best_d = a;
+    for (int c = 1; c <= 0xFE; ++c) {
+        double d = fabs(a - oracle_ue5m3_decode(c));
+        if (d < best_d || (d == best_d && (c & 1) == 0)) { best = c; best_d = d; }
+    }
+    return best;
 }
 
 /* MXFP4 abs-max scale ([MR-GPTQ] section 1: power-of-two rounding of the
@@ -263,7 +300,8 @@ static int scale_usable(float S) { return !isnan(S) && !isinf(S) && !(S < 0.0f);
 /* Effective scale S = fl(dec(code) * g); the decoded value is exact in fp32. */
 static float effective_scale(int fmt, int code, float g)
 {
-    double d = (fmt == SF_E8M0) ? oracle_e8m0_decode(code) : oracle_e4m3_decode(code);
+    double d = (fmt == SF_E8M0) ? oracle_e8m0_decode(code)
+             : (fmt == SF_E4M3) ? oracle_e4m3_decode(code) : oracle_ue5m3_decode(code);
     return (float)d * g;
 }
 
@@ -313,7 +351,7 @@ static int choose_scale(int fmt, int strategy, const float* y, int B, float g, i
     if (strategy == ST_GIVEN) return (fmt == SF_E4M3) ? (given & 0x7F) : given;
     uint32_t ab_bits = block_amax_bits(y, B);
     float a_b = f32_of_bits(ab_bits);
-    int nan_code = (fmt == SF_E8M0) ? E8M0_NAN_CODE : E4M3_NAN_CODE;
+    int nan_code = (fmt == SF_E8M0) ? E8M0_NAN_CODE : (fmt == SF_E4M3) ? E4M3_NAN_CODE : UE5M3_NAN_CODE;
     if (ab_bits >= 0x7F800000u || isnan(g) || isinf(g)) return nan_code;
 
     if (fmt == SF_E8M0) {
@@ -330,10 +368,12 @@ static int choose_scale(int fmt, int strategy, const float* y, int B, float g, i
         return oracle_e8m0_absmax_code(a_b);
     }
 
-    /* E4M3: abs-max maps the block maximum onto 6 = the largest E2M1 value,
-     * rounded to the nearest E4M3 value. */
+    /* E4M3 (and UE5M3): abs-max maps the block maximum onto 6 = the largest
+     * E2M1 value, rounded to the nearest scale value. */
+    int (*encode)(float) = (fmt == SF_E4M3) ? oracle_e4m3_encode : oracle_ue5m3_encode;
+    int top_code = (fmt == SF_E4M3) ? 0x7E : 0xFE;
     float six_g = 6.0f * g;
-    int s6 = oracle_e4m3_encode(a_b / six_g);
+    int s6 = encode(a_b / six_g);
     switch (strategy) {
     case ST_ABSMAX:
         return s6;
@@ -341,15 +381,15 @@ static int choose_scale(int fmt, int strategy, const float* y, int B, float g, i
         return s6 < 1 ? 1 : s6;
     case ST_FOUR_OVER_SIX: {              /* map the maximum to 6 or to 4 */
         float four_g = 4.0f * g;
-        int s4 = oracle_e4m3_encode(a_b / four_g);
+        int s4 = encode(a_b / four_g);
         float sse6 = oracle_block_sse(y, B, effective_scale(fmt, s6, g));
         float sse4 = oracle_block_sse(y, B, effective_scale(fmt, s4, g));
         return (sse4 < sse6) ? s4 : s6;  /* equal error keeps the smaller code */
     }
-    case ST_BRUTE_FORCE: {                /* every positive finite E4M3 scale */
+    case ST_BRUTE_FORCE: {                /* every positive finite scale */
         int best = -1;
         float best_sse = 0.0f;
-        for (int c = 1; c <= 0x7E; ++c) {
+        for (int c = 1; c <= top_code; ++c) {
             float sse = oracle_block_sse(y, B, effective_scale(fmt, c, g));
             if (best < 0 || sse < best_sse) { best = c; best_sse = sse; }
         }
@@ -482,6 +522,7 @@ int oracle_quantize(int fmt, int B, int strategy, int global_mode, float user_g,
     if (H != 0 && H != 16 && H != 32) return -1;
     if (cols % B || (H && cols % H) || cols % 2) return -1;
     if (fmt == SF_E8M0 && (global_mode != GM_NONE || strategy == ST_FOUR_OVER_SIX)) return -1;
+    if (fmt == SF_UE5M3 && global_mode != GM_NONE && global_mode != GM_USER) return -1;
     if (strategy == ST_GIVEN && (!scales || global_mode == GM_SEARCH)) return -1;
 
     float* y = widen_and_rotate(x, x_dt, rows, cols, ld_x, H);
@@ -501,7 +542,7 @@ int oracle_quantize(int fmt, int B, int strategy, int global_mode, float user_g,
             int code = choose_scale(fmt, strategy, yb, B, g, given);
             if (scales && strategy != ST_GIVEN) scales[r * nb + j] = (uint8_t)code;
 
-            int nan_code = (fmt == SF_E8M0) ? E8M0_NAN_CODE : E4M3_NAN_CODE;
+            int nan_code = (fmt == SF_E8M0) ? E8M0_NAN_CODE : (fmt == SF_E4M3) ? E4M3_NAN_CODE : UE5M3_NAN_CODE;
             float S = (code == nan_code) ? canonical_nan(0) : effective_scale(fmt, code, g);
             int usable = scale_usable(S);
 
@@ -550,7 +591,7 @@ static float decode_elem(int q, float S)
 static float stored_scale(int fmt, int code, float g)
 {
     if (fmt == SF_E4M3) code &= 0x7F;
-    int nan_code = (fmt == SF_E8M0) ? E8M0_NAN_CODE : E4M3_NAN_CODE;
+    int nan_code = (fmt == SF_E8M0) ? E8M0_NAN_CODE : (fmt == SF_E4M3) ? E4M3_NAN_CODE : UE5M3_NAN_CODE;
     if (code == nan_code) return canonical_nan(0);
     return effective_scale(fmt, code, g);
 }

@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "liboracle_fp4q.so")
 ALT_LIB = os.environ.get("FP4Q_ORACLE_LIB")
 
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
-SF_E8M0, SF_E4M3 = 0, 1
+SF_E8M0, SF_E4M3, SF_UE5M3 = 0, 1, 2
 ABSMAX, PREVENT_ZERO, FOUR_OVER_SIX, BRUTE_FORCE, GIVEN = 0, 1, 2, 3, 4
 GLOBAL_NONE, GLOBAL_TENSOR_AMAX, GLOBAL_USER, GLOBAL_SEARCH = 0, 1, 2, 3
 SEARCH_CANDIDATES = 32
@@ -56,6 +56,8 @@ def lib():
         L.oracle_e4m3_decode.argtypes, L.oracle_e4m3_decode.restype = [i], ctypes.c_double
         L.oracle_e4m3_encode.argtypes, L.oracle_e4m3_encode.restype = [f], i
         L.oracle_e8m0_decode.argtypes, L.oracle_e8m0_decode.restype = [i], ctypes.c_double
+        L.oracle_ue5m3_decode.argtypes, L.oracle_ue5m3_decode.restype = [i], ctypes.c_double
+        L.oracle_ue5m3_encode.argtypes, L.oracle_ue5m3_encode.restype = [f], i
         L.oracle_e8m0_absmax_code.argtypes, L.oracle_e8m0_absmax_code.restype = [f], i
         L.oracle_bf16_to_f32.argtypes, L.oracle_bf16_to_f32.restype = [ctypes.c_uint16], f
         L.oracle_f16_to_f32.argtypes, L.oracle_f16_to_f32.restype = [ctypes.c_uint16], f
@@ -117,6 +119,14 @@ def e4m3_decode(code: int) -> float:
 
 def e4m3_encode(v) -> int:
     return lib().oracle_e4m3_encode(float(np.float32(v)))
+
+
+def ue5m3_decode(code: int) -> float:
+    return lib().oracle_ue5m3_decode(int(code))
+
+
+def ue5m3_encode(v) -> int:
+    return lib().oracle_ue5m3_encode(float(np.float32(v)))
 
 
 def e8m0_decode(code: int) -> float:

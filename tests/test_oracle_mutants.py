@@ -25,7 +25,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "fp4q_oracle.c")
 PIN_FILES = ["test_oracle_formats.py", "test_oracle_quant.py", "test_oracle_golden.py",
-             "test_oracle_rotation.py", "test_oracle_focus.py", "test_oracle_search.py"]
+             "test_oracle_rotation.py", "test_oracle_focus.py", "test_oracle_search.py",
+             "test_oracle_ue5m3.py"]
 
 # (name, text in the oracle, replacement, which occurrence (1-based))
 MUTANTS = [
@@ -53,12 +54,17 @@ MUTANTS = [
      "uint32_t b = bits_of_f32(y[i]);\n        if (b > m) m = b;\n    }\n    return m;", 1),
     ("global scale without the 6", "f32_of_bits(m) / 2688.0f", "f32_of_bits(m) / 448.0f", 1),
     ("zero tensor keeps g = 0", "return (g == 0.0f) ? 1.0f : g;", "return g;", 1),
-    ("abs-max divides by 4", "int s6 = oracle_e4m3_encode(a_b / six_g);",
-     "int s6 = oracle_e4m3_encode(a_b / (4.0f * g));", 1),
+    ("abs-max divides by 4", "int s6 = encode(a_b / six_g);", "int s6 = encode(a_b / (4.0f * g));", 1),
     ("prevent-zero missing", "return s6 < 1 ? 1 : s6;", "return s6;", 1),
     ("4-over-6 ties to s4", "return (sse4 < sse6) ? s4 : s6;", "return (sse4 <= sse6) ? s4 : s6;", 1),
-    ("brute force skips 448", "for (int c = 1; c <= 0x7E; ++c) {\n            float sse",
-     "for (int c = 1; c < 0x7E; ++c) {\n            float sse", 1),
+    ("brute force skips 448", "int top_code = (fmt == SF_E4M3) ? 0x7E : 0xFE;",
+     "int top_code = (fmt == SF_E4M3) ? 0x7D : 0xFE;", 1),
+    ("ue5m3 exponent bias", "ldexp(1.0, e - 15)", "ldexp(1.0, e - 14)", 1),
+    ("ue5m3 subnormal step", "m * ldexp(1.0, -17)", "m * ldexp(1.0, -18)", 1),
+    ("ue5m3 tie to odd", "if (d < best_d || (d == best_d && (c & 1) == 0)) { best = c; best_d = d; }\n    }\n    return best;\n}\n\n/* MXFP4",
+     "if (d < best_d || (d == best_d && (c & 1) == 1)) { best = c; best_d = d; }\n    }\n    return best;\n}\n\n/* MXFP4", 1),
+    ("ue5m3 brute force skips the top code", "int top_code = (fmt == SF_E4M3) ? 0x7E : 0xFE;",
+     "int top_code = (fmt == SF_E4M3) ? 0x7E : 0xFD;", 1),
     ("brute force ties to larger code", "if (best < 0 || sse < best_sse) { best = c; best_sse = sse; }",
      "if (best < 0 || sse <= best_sse) { best = c; best_sse = sse; }", 2),
     ("mse divides by B - 1", "float m = sse / (float)B;", "float m = sse / (float)(B - 1);", 1),
