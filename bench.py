@@ -277,22 +277,22 @@ def build_step(F, S, torch, dev):
     return calls, keep, host, X
 
 
-def time_search(F, torch, x, reps=5):
-    """The MSE-searched per-tensor scale (a widening beyond the step): NVFP4
-    block 16 on one 4096 x 4096 input, abs-max and 4-over-6 inside, every
-    output, timed per call with HIP events on the library's stream."""
+def time_quantize_configs(F, torch, x, cfgs, reps=5):
+    """Quantize calls outside the step (widenings of the path): each config on
+    one 4096 x 4096 fp32 input with every output, timed per call with HIP
+    events on the library's stream; GB/s of the call's algorithmic bytes."""
     L = F.lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     R, C = x.shape
     out = {}
-    for name, st in (("absmax", F.ABSMAX), ("4-over-6", F.FOUR_OVER_SIX)):
-        cfg = F.config(F.E4M3, 16, st, F.GLOBAL_SEARCH)
+    for name, cfg in cfgs:
+        B = cfg.block
         codes = torch.empty((R, C // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((R, C // 16), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((R, C // B), dtype=torch.uint8, device=x.device)
         g = torch.empty(1, dtype=torch.float32, device=x.device)
         dq = torch.empty((R, C), dtype=torch.float32, device=x.device)
-        mse = torch.empty((R, C // 16), dtype=torch.float32, device=x.device)
-        ws = torch.empty(F.workspace_bytes(cfg, R, C), dtype=torch.uint8, device=x.device)
+        mse = torch.empty((R, C // B), dtype=torch.float32, device=x.device)
+        ws = torch.empty(max(F.workspace_bytes(cfg, R, C), 16), dtype=torch.uint8, device=x.device)
         args = (ctypes.byref(cfg), ctypes.c_void_p(x.data_ptr()), F.F32, R, C, C, ctypes.c_void_p(codes.data_ptr()),
                 ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(dq.data_ptr()),
                 F.F32, C, ctypes.c_void_p(mse.data_ptr()), ctypes.c_void_p(ws.data_ptr()), stream)
@@ -304,11 +304,11 @@ def time_search(F, torch, x, reps=5):
             st_ = L.fp4q_quantize(*args)
             e1.record()
             if st_ != 0:
-                raise RuntimeError(f"search quantize: status {st_}")
+                raise RuntimeError(f"{name}: status {st_}")
             ev.append((e0, e1))
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev[1:]]))
-        nb = quant_bytes(R, C, 16)
+        nb = quant_bytes(R, C, B)
         out[name] = {"ms": round(ms, 4), "GB/s": round(nb / (ms * 1e6), 1),
                      "Gelem/s": round(R * C / (ms * 1e6), 2), "g": float(g.item())}
     return out
@@ -487,7 +487,11 @@ def main():
     del dsts
     for k, v in breakdown.items():
         v["frac_of_copy"] = round(v["GB/s"] / copy_gbs, 4)
-    search = time_search(F, torch, X["normal"])
+    search = time_quantize_configs(F, torch, X["normal"], [
+        ("absmax", F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_SEARCH)),
+        ("4-over-6", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_SEARCH))])
+    ue5m3 = time_quantize_configs(F, torch, X["normal"], [
+        (f"B={B} {STRATS[st]}", F.config(F.UE5M3, B, st)) for B in (16, 4) for st in (0, 2, 3)])
     stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
     sb = sum(c.nbytes for c, _ in stream_quant)
     sms = sum(ms for _, ms in stream_quant)
@@ -520,6 +524,8 @@ def main():
                                                  "candidates (abs-max pre-pass, 32-candidate scoring, tree "
                                                  "reduction, pick, quantize at the winner); GB/s of the "
                                                  "quantize call's algorithmic bytes"),
+        "ue5m3_scales": dict(ue5m3, what="not part of the step: quantize of the 4096x4096 N(0,1) input with "
+                                         "UE5M3 block scales (no per-tensor scale), every output"),
         "copy_reference": {"GB/s": round(copy_gbs, 1), "hbm_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
                            "what": "device copy (read + write bytes) of the four 64 MiB inputs in rotation, "
                                    "the same access pattern as the quantize calls; per_strategy frac_of_copy "

@@ -27,11 +27,11 @@
  *            sign (bit 3) and E2M1 magnitude code 0..7 for
  *            {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
  *  - scales: [rows, cols/block] bytes, dense, row-major; E8M0 (value
- *            2^(code-127), 0xFF = NaN) or unsigned OCP E4M3 (bit 7 ignored,
- *            0x7F = NaN, largest 448).
+ *            2^(code-127), 0xFF = NaN), unsigned OCP E4M3 (bit 7 ignored,
+ *            0x7F = NaN, largest 448) or UE5M3 (below).
  *  - g:      the per-tensor fp32 scale of hierarchical scaling; the
  *            effective block scale is S = fl(decode(code) * g).  For E8M0
- *            there is no g (it is 1).
+ *            there is no g (it is 1); UE5M3 takes g from NONE or USER only.
  *  - Every buffer is device memory the caller allocated (the library
  *    allocates nothing and keeps no state).  Base pointers must be 16-byte
  *    aligned, and ld * element_size must be a multiple of 16 bytes, as must
@@ -73,16 +73,24 @@ typedef enum {
 
 typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1, FP4Q_F16 = 2 } fp4q_dtype;
 
-typedef enum { FP4Q_SCALE_E8M0 = 0, FP4Q_SCALE_E4M3 = 1 } fp4q_scale_fmt;
+/* Block scale formats.  UE5M3 is the unsigned wide-exponent scale the
+ * "Finer is Better" page compares with E4M3 + hierarchical scaling +
+ * 4-over-6 (key findings); the page gives no encoding, so this library reads
+ * it as 5 exponent bits with bias 15 and 3 mantissa bits: (1 + m/8) 2^(e-15),
+ * subnormals m 2^-17, largest 0xFE = 114688, 0xFF = NaN, no infinities,
+ * round-half-to-even with saturation.  It needs no per-tensor scale: global
+ * modes NONE and USER. */
+typedef enum { FP4Q_SCALE_E8M0 = 0, FP4Q_SCALE_E4M3 = 1, FP4Q_SCALE_UE5M3 = 2 } fp4q_scale_fmt;
 
 /* Scale strategies ("Finer is Better (with the Right Scaling)", method
  * part 2).  ABSMAX maps the block abs-max onto 6 and rounds the scale to the
  * format (E8M0: the power of two 2^(floor(log2 amax) - 2)); PREVENT_ZERO is
  * ABSMAX with an E4M3 code of 0 raised to the smallest nonzero code;
  * FOUR_OVER_SIX keeps whichever of the map-to-6 and map-to-4 scales gives
- * the lower block squared error (E4M3 only); BRUTE_FORCE tries every
- * positive finite scale (126 E4M3 codes, 255 E8M0 codes) and keeps the
- * lowest squared error, ties to the smaller code; GIVEN reads the scales. */
+ * the lower block squared error (E4M3, UE5M3); BRUTE_FORCE tries every
+ * positive finite scale (126 E4M3 codes, 255 E8M0 codes, 254 UE5M3 codes)
+ * and keeps the lowest squared error, ties to the smaller code; GIVEN reads
+ * the scales. */
 typedef enum {
     FP4Q_ABSMAX = 0,
     FP4Q_PREVENT_ZERO = 1,
@@ -94,7 +102,8 @@ typedef enum {
 /* Per-tensor scale g (hierarchical scaling, same page, method part 2):
  * NONE -> g = 1; TENSOR_AMAX -> g = fl(amax(|x|) / 2688) over the whole
  * (rotated) tensor, 2688 = 6 * 448, and g = 1 when that is 0, NaN when the
- * tensor holds NaN or infinity; USER -> g = global_scale.  E4M3 only.
+ * tensor holds NaN or infinity; USER -> g = global_scale.  TENSOR_AMAX and
+ * SEARCH: E4M3 only; USER: E4M3 and UE5M3.
  * SEARCH (per-tensor scale chosen for minimum MSE, MR-GPTQ page, section
  * 2.2): with g0 the TENSOR_AMAX scale, the candidates g_j = fl(g0 (1 - j/64)),
  * j = 0..31, are each scored by the fp64 balanced-tree sum, over all blocks

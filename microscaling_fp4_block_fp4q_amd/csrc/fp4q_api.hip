@@ -27,7 +27,9 @@ int grid_for(int64_t units) {
 // Checks of the configuration shared by every call.
 fp4q_status check_config(const fp4q_config* cfg) {
     if (!cfg || cfg->struct_size != sizeof(fp4q_config)) return FP4Q_ERR_INVALID_ARG;
-    if (cfg->scale_fmt != FP4Q_SCALE_E8M0 && cfg->scale_fmt != FP4Q_SCALE_E4M3) return FP4Q_ERR_INVALID_ARG;
+    if (cfg->scale_fmt != FP4Q_SCALE_E8M0 && cfg->scale_fmt != FP4Q_SCALE_E4M3 &&
+        cfg->scale_fmt != FP4Q_SCALE_UE5M3)
+        return FP4Q_ERR_INVALID_ARG;
     if (cfg->strategy < FP4Q_ABSMAX || cfg->strategy > FP4Q_GIVEN) return FP4Q_ERR_INVALID_ARG;
     if (cfg->global_mode < FP4Q_GLOBAL_NONE || cfg->global_mode > FP4Q_GLOBAL_SEARCH) return FP4Q_ERR_INVALID_ARG;
     if (cfg->hadamard < 0) return FP4Q_ERR_INVALID_ARG;
@@ -35,6 +37,9 @@ fp4q_status check_config(const fp4q_config* cfg) {
     if (cfg->hadamard != 0 && cfg->hadamard != 16 && cfg->hadamard != 32) return FP4Q_ERR_UNSUPPORTED;
     if (cfg->scale_fmt == FP4Q_SCALE_E8M0 &&
         (cfg->global_mode != FP4Q_GLOBAL_NONE || cfg->strategy == FP4Q_FOUR_OVER_SIX))
+        return FP4Q_ERR_UNSUPPORTED;
+    if (cfg->scale_fmt == FP4Q_SCALE_UE5M3 &&
+        (cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX || cfg->global_mode == FP4Q_GLOBAL_SEARCH))
         return FP4Q_ERR_UNSUPPORTED;
     if (cfg->global_mode == FP4Q_GLOBAL_SEARCH &&
         (cfg->strategy == FP4Q_BRUTE_FORCE || cfg->strategy == FP4Q_GIVEN))

@@ -19,7 +19,7 @@
 namespace fp4q_dev {
 
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
-enum : int { SF_E8M0 = 0, SF_E4M3 = 1 };
+enum : int { SF_E8M0 = 0, SF_E4M3 = 1, SF_UE5M3 = 2 };
 enum : int { ST_ABSMAX = 0, ST_PREVENT_ZERO = 1, ST_FOUR_OVER_SIX = 2, ST_BRUTE_FORCE = 3, ST_GIVEN = 4 };
 // Per-tensor scale modes of the kernels; GM_DEVICE reads g from device
 // memory (the searched scale).
@@ -28,6 +28,7 @@ enum : int { GM_NONE = 0, GM_TENSOR_AMAX = 1, GM_USER = 2, GM_DEVICE = 3 };
 constexpr uint32_t kQNaN = 0x7FC00000u;
 constexpr uint32_t kE4M3NaN = 0x7Fu;
 constexpr uint32_t kE8M0NaN = 0xFFu;
+constexpr uint32_t kUE5M3NaN = 0xFFu;
 
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
@@ -90,6 +91,45 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
     float r = __builtin_rintf(q);
     return (uint32_t)((e + 7) * 8 - 8) + (uint32_t)r;
 }
+
+// UE5M3, the unsigned wide-exponent scale of the Finer-is-Better page (key
+// findings), read as 5 exponent bits with bias 15 and 3 mantissa bits:
+// (1 + m/8) 2^(e-15), or m 2^-17 for e = 0; codes 0..0xFE, 0xFF is NaN.
+__device__ __forceinline__ float ue5m3_value(uint32_t code) {
+    uint32_t e = code >> 3, m = code & 7u;
+    return e ? as_f(((e + 112u) << 23) | (m << 20)) : (float)m * 0x1p-17f;
+}
+
+// Nearest UE5M3 code of v >= 0 (may be +inf, not NaN), ties to the even
+// code, saturating at 0xFE = 1.75 * 2^16; the same exact scaling and
+// half-to-even rint as e4m3_encode, with subnormals sharing e = -14.
+__device__ __forceinline__ uint32_t ue5m3_encode(float v) {
+    if (!(v < 114688.0f)) return 0xFEu;
+    int e = max((int)(as_u(v) >> 23) - 127, -14);
+    float q = __builtin_ldexpf(v, 3 - e);
+    float r = __builtin_rintf(q);
+    return (uint32_t)((e + 15) * 8 - 8) + (uint32_t)r;
+}
+
+// The non-power-of-two scale formats (E4M3, UE5M3) behind one interface.
+template <int SF>
+__device__ __forceinline__ float scale_value(uint32_t code) {
+    if constexpr (SF == SF_E4M3) return e4m3_value(code);
+    else return ue5m3_value(code);
+}
+template <int SF>
+__device__ __forceinline__ uint32_t scale_encode(float v) {
+    if constexpr (SF == SF_E4M3) return e4m3_encode(v);
+    else return ue5m3_encode(v);
+}
+template <int SF>
+constexpr uint32_t scale_nan() { return SF == SF_E8M0 ? kE8M0NaN : (SF == SF_E4M3 ? kE4M3NaN : kUE5M3NaN); }
+// Bits of a stored code that carry the scale (E4M3 scales are unsigned: bit 7 is ignored).
+template <int SF>
+constexpr uint32_t scale_code_mask() { return SF == SF_E4M3 ? 0x7Fu : 0xFFu; }
+// Largest finite code.
+template <int SF>
+constexpr uint32_t scale_top() { return SF == SF_E4M3 ? 0x7Eu : 0xFEu; }
 
 // E8M0 scale 2^(code-127) and its exact reciprocal 2^(127-code), code 0..254
 // (2^-127 is the fp32 subnormal 0x00400000).

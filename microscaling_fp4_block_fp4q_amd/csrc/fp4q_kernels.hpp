@@ -242,12 +242,13 @@ __device__ __forceinline__ float encode_block(const float (&y)[U], float S, floa
     return tree_sum<B>(e);
 }
 
-// encode_block at an E4M3 scale chosen per lane: division-free when S is in
-// range, IEEE division otherwise (extreme g).  A zero scale with finite
-// elements also takes the division-free path with R = 0, which yields the
-// quotient 0 that a zero scale defines (q0 = 0, residual a, correction 0).
+// encode_block at a scale chosen per lane that need not be a power of two
+// (E4M3 or UE5M3 times g): division-free when S is in range, IEEE division
+// otherwise (extreme g).  A zero scale with finite elements also takes the
+// division-free path with R = 0, which yields the quotient 0 that a zero
+// scale defines (q0 = 0, residual a, correction 0).
 template <int B, int OFF, bool NAN_GUARD, int U>
-__device__ __forceinline__ float encode_block_e4m3(const float (&y)[U], float S, float (&r)[B]) {
+__device__ __forceinline__ float encode_block_at(const float (&y)[U], float S, float (&r)[B]) {
     const bool zero = !NAN_GUARD && S == 0.0f;
     if (fast_quotient_range(S) || zero)
         return encode_block<SF_E4M3, B, OFF, NAN_GUARD, true>(y, S, zero ? 0.0f : 1.0f / S, r);
@@ -280,14 +281,14 @@ __device__ __forceinline__ float zero_bin_limit(float S) {
 
 template <int SF>
 __device__ __forceinline__ void fill_bf_table(BfTable& t, float g) {
-    constexpr uint32_t N = SF == SF_E8M0 ? 255u : 127u;
+    constexpr uint32_t N = SF == SF_E8M0 ? 255u : scale_top<SF>() + 1u;
     for (uint32_t c = threadIdx.x; c < N; c += kThreads) {
         float S, R;
         if constexpr (SF == SF_E8M0) {
             S = e8m0_value(c);
             R = e8m0_inverse(c);
         } else {
-            S = e4m3_value(c) * g;
+            S = scale_value<SF>(c) * g;
             R = fast_quotient_range(S) ? 1.0f / S : 0.0f;
         }
         t.sr[c] = make_float2(S, R);
@@ -297,7 +298,8 @@ __device__ __forceinline__ void fill_bf_table(BfTable& t, float g) {
     // whole number of candidates (their results are discarded)
     for (uint32_t c = N + threadIdx.x; c < 256u + BfTable::kPad; c += kThreads) t.sr[c] = make_float2(1.0f, 1.0f);
     if (threadIdx.x == 0)
-        t.fast = SF == SF_E8M0 || (fast_quotient_range(e4m3_value(1u) * g) && fast_quotient_range(e4m3_value(0x7Eu) * g));
+        t.fast = SF == SF_E8M0 || (fast_quotient_range(scale_value<SF>(1u) * g) &&
+                                   fast_quotient_range(scale_value<SF>(scale_top<SF>()) * g));
     __syncthreads();
 }
 
@@ -368,7 +370,7 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
                                                         uint32_t c_second, float g, float six_g, const BfTable& t,
                                                         uint32_t& c_lo, uint32_t& c_hi) {
     constexpr uint32_t CLO = SF == SF_E8M0 ? 0u : 1u;           // candidate codes [CLO, CEND)
-    constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : 127u;
+    constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : scale_top<SF>() + 1u;
     // every element encodes to zero at the smallest scale: all codes tie
     if (a_b <= t.t0[CLO]) {
         c_lo = c_hi = CLO;
@@ -388,7 +390,7 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
     // fl(6 S_c), computed the way the encoder computes it (grid value 6 times S_c)
     auto six_s = [&](uint32_t c) {
         if constexpr (SF == SF_E8M0) return 6.0f * e8m0_value(c);
-        else return 6.0f * (e4m3_value(c) * g);
+        else return 6.0f * (scale_value<SF>(c) * g);
     };
 
     // upper end: first code past c_best whose zero-bin bound exceeds best0, or
@@ -405,7 +407,7 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
     };
     uint32_t guess_hi;
     if constexpr (SF == SF_E8M0) guess_hi = c_best + 3u;
-    else guess_hi = e4m3_encode(a_b / g) + 16u;           // around where a_max / S drops near 0.25 * 4
+    else guess_hi = scale_encode<SF>(a_b / g) + 16u;      // around where a_max / S drops near 0.25 * 4
     c_hi = first_true_from(c_best + 1u, CEND, guess_hi, stop_up);
     if (c_hi < CEND && a_b <= t.t0[c_hi]) ++c_hi;
 
@@ -418,7 +420,7 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
     };
     uint32_t guess_lo;
     if constexpr (SF == SF_E8M0) guess_lo = c_star > CLO ? c_star - 1u : CLO;
-    else guess_lo = e4m3_encode(fmaxf(a_b - __builtin_sqrtf(best0), 0.0f) / six_g);
+    else guess_lo = scale_encode<SF>(fmaxf(a_b - __builtin_sqrtf(best0), 0.0f) / six_g);
     c_lo = first_true_from(CLO, c_star, guess_lo, keep_lo);
     return best;
 }
@@ -469,10 +471,10 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
             S = e8m0_value(sc);
             if (!nan_block) sse = encode_block<SF, B, OFF, true, true>(y, S, e8m0_inverse(sc), r);
         } else {
-            sc = given & 0x7Fu;
-            S = e4m3_value(sc) * g;
-            nan_block = sc == kE4M3NaN || !scale_usable(S);
-            if (!nan_block) sse = encode_block_e4m3<B, OFF, true>(y, S, r);
+            sc = given & scale_code_mask<SF>();
+            S = scale_value<SF>(sc) * g;
+            nan_block = sc == scale_nan<SF>() || !scale_usable(S);
+            if (!nan_block) sse = encode_block_at<B, OFF, true>(y, S, r);
         }
     } else {
         uint32_t ab = 0;
@@ -486,18 +488,18 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
                 S = e8m0_value(sc);
                 sse = encode_block<SF, B, OFF, false, true>(y, S, e8m0_inverse(sc), r);
             } else {
-                const uint32_t s6 = e4m3_encode(a_b / six_g);
+                const uint32_t s6 = scale_encode<SF>(a_b / six_g);
                 if constexpr (ST == ST_ABSMAX) {
                     sc = (prevent_zero && s6 == 0u) ? 1u : s6;
-                    S = e4m3_value(sc) * g;
-                    sse = encode_block_e4m3<B, OFF, false>(y, S, r);
+                    S = scale_value<SF>(sc) * g;
+                    sse = encode_block_at<B, OFF, false>(y, S, r);
                 } else {
                     static_assert(ST == ST_FOUR_OVER_SIX, "brute force has its own kernel");
-                    const uint32_t s4 = e4m3_encode(a_b / four_g);
-                    const float S6 = e4m3_value(s6) * g, S4 = e4m3_value(s4) * g;
+                    const uint32_t s4 = scale_encode<SF>(a_b / four_g);
+                    const float S6 = scale_value<SF>(s6) * g, S4 = scale_value<SF>(s4) * g;
                     float r4[B];
-                    const float e6 = encode_block_e4m3<B, OFF, false>(y, S6, r);
-                    const float e4 = encode_block_e4m3<B, OFF, false>(y, S4, r4);
+                    const float e6 = encode_block_at<B, OFF, false>(y, S6, r);
+                    const float e4 = encode_block_at<B, OFF, false>(y, S4, r4);
                     const bool take4 = e4 < e6;   // equal error keeps the smaller code s6
                     sc = take4 ? s4 : s6;
                     S = take4 ? S4 : S6;
@@ -507,7 +509,7 @@ __device__ __forceinline__ void quant_block(const float (&y)[U], float g, float 
                 }
             }
         } else {
-            sc = SF == SF_E8M0 ? kE8M0NaN : kE4M3NaN;
+            sc = scale_nan<SF>();
         }
     }
 
@@ -744,12 +746,12 @@ __device__ __forceinline__ float block_score(const float (&y)[U], uint32_t ab, f
     float r[B];
     if constexpr (ST == ST_ABSMAX) {
         const uint32_t sc = (prevent_zero && s6 == 0u) ? 1u : s6;
-        return encode_block_e4m3<B, OFF, false>(y, e4m3_value(sc) * g, r);
+        return encode_block_at<B, OFF, false>(y, e4m3_value(sc) * g, r);
     } else {
         static_assert(ST == ST_FOUR_OVER_SIX, "abs-max, prevent-zero or 4-over-6");
         const uint32_t s4 = e4m3_encode(a_b / four_g);
-        const float e6 = encode_block_e4m3<B, OFF, false>(y, e4m3_value(s6) * g, r);
-        const float e4 = encode_block_e4m3<B, OFF, false>(y, e4m3_value(s4) * g, r);
+        const float e6 = encode_block_at<B, OFF, false>(y, e4m3_value(s6) * g, r);
+        const float e4 = encode_block_at<B, OFF, false>(y, e4m3_value(s4) * g, r);
         return e4 < e6 ? e4 : e6;
     }
 }
@@ -866,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
     constexpr int NB = U / B;
     constexpr int SLOT = slot_bytes<U>();
     constexpr int NBLK = kTileUnits * NB;
-    constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : 127u;
+    constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : scale_top<SF>() + 1u;
     constexpr int K = B >= 16 ? 1 : 16 / B;       // candidates of one block per work item
     // an item reads codes c0 .. c0 + K - 1 with c0 < CEND
     static_assert(CEND + K - 1 <= 256 + BfTable::kPad, "items read past the table");
@@ -938,7 +940,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                     c1 = e8m0_absmax_code(ab);
                     c2 = c1 < 254u ? c1 + 1u : c1;
                 } else {
-                    const uint32_t s6 = e4m3_encode(a_b / six_g), s4 = e4m3_encode(a_b / four_g);
+                    const uint32_t s6 = scale_encode<SF>(a_b / six_g), s4 = scale_encode<SF>(a_b / four_g);
                     c1 = s6 > 0u ? s6 : 1u;
                     c2 = s4 > 0u ? s4 : 1u;
                 }
@@ -1038,7 +1040,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             float r[B];
             float S = 0.0f;
             if (nan_blk[b]) {
-                sc[b] = SF == SF_E8M0 ? kE8M0NaN : kE4M3NaN;
+                sc[b] = scale_nan<SF>();
                 sse[b] = as_f(kQNaN);
 #pragma unroll
                 for (int i = 0; i < B; ++i) r[i] = 0.0f;
@@ -1050,13 +1052,31 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                     sse[b] = encode_block<SF, B, OFF, false, true>(y, S, e8m0_inverse(c), r);
                 } else {
                     S = s_bf.sr[c].x;
-                    sse[b] = encode_block_e4m3<B, OFF, false>(y, S, r);
+                    sse[b] = encode_block_at<B, OFF, false>(y, S, r);
                 }
             }
             finish_block<B, OFF>(y, r, S, nan_blk[b], cw, sink);
         });
         store_unit_outputs<B, U>(p, u0, nvalid, lane, W.tile, cw, sc, sse, true);
     }
+}
+
+// Scale of a stored block code (runtime format) times g; usable is false
+// for the NaN code and for scales that are NaN, infinite or negative.
+__device__ __forceinline__ float stored_scale(int fmt, uint32_t code, float g, bool& usable) {
+    if (fmt == SF_E8M0) {
+        usable = code != kE8M0NaN;
+        return e8m0_value(code);
+    }
+    if (fmt == SF_E4M3) {
+        const uint32_t c7 = code & 0x7Fu;
+        const float S = e4m3_value(c7) * g;
+        usable = c7 != kE4M3NaN && scale_usable(S);
+        return S;
+    }
+    const float S = ue5m3_value(code) * g;
+    usable = code != kUE5M3NaN && scale_usable(S);
+    return S;
 }
 
 // Dequantize codes + scales.  One lane per DU consecutive output values
@@ -1076,15 +1096,9 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DequantArgs p) {
         bool nan_block[NBD];
 #pragma unroll
         for (int b = 0; b < NBD; ++b) {
-            const uint32_t code = p.scales[e0 / B + b];
-            if (p.scale_fmt == SF_E8M0) {
-                nan_block[b] = code == kE8M0NaN;
-                S[b] = e8m0_value(code);
-            } else {
-                const uint32_t c7 = code & 0x7Fu;
-                S[b] = e4m3_value(c7) * g;
-                nan_block[b] = c7 == kE4M3NaN || !scale_usable(S[b]);
-            }
+            bool usable;
+            S[b] = stored_scale(p.scale_fmt, p.scales[e0 / B + b], g, usable);
+            nan_block[b] = !usable;
         }
         float v[DU];
 #pragma unroll
@@ -1118,17 +1132,9 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MseArgs p) {
         load_codes<U>(p.codes + u * (U / 2), c);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const uint32_t code = p.scales[u * NB + b];
-            float S;
-            bool nan_block;
-            if (p.scale_fmt == SF_E8M0) {
-                nan_block = code == kE8M0NaN;
-                S = e8m0_value(code);
-            } else {
-                const uint32_t c7 = code & 0x7Fu;
-                S = e4m3_value(c7) * g;
-                nan_block = c7 == kE4M3NaN || !scale_usable(S);
-            }
+            bool usable;
+            const float S = stored_scale(p.scale_fmt, p.scales[u * NB + b], g, usable);
+            const bool nan_block = !usable;
             float e[B];
 #pragma unroll
             for (int i = 0; i < B; ++i) {
@@ -1141,18 +1147,6 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MseArgs p) {
             p.mse[u * NB + b] = (nan_block || m != m) ? as_f(kQNaN) : m;
         }
     }
-}
-
-// Scale of block `code` for the FOCUS kernels.
-__device__ __forceinline__ float stored_scale(int fmt, uint32_t code, float g, bool& usable) {
-    if (fmt == SF_E8M0) {
-        usable = code != kE8M0NaN;
-        return e8m0_value(code);
-    }
-    const uint32_t c7 = code & 0x7Fu;
-    const float S = e4m3_value(c7) * g;
-    usable = c7 != kE4M3NaN && scale_usable(S);
-    return S;
 }
 
 __device__ __forceinline__ float f16_value(uint16_t h) { return f16_bits_to_f32(h); }

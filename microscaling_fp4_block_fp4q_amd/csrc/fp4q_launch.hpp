@@ -70,7 +70,7 @@ hipError_t dispatch_quant_st(const QuantArgs& a, int st, int grid, hipStream_t s
     case ST_PREVENT_ZERO:
         return launch_quant_t<InT, B, H, SF, ST_ABSMAX>(a, grid, s);
     case ST_FOUR_OVER_SIX:
-        if constexpr (SF == SF_E4M3) return launch_quant_t<InT, B, H, SF, ST_FOUR_OVER_SIX>(a, grid, s);
+        if constexpr (SF != SF_E8M0) return launch_quant_t<InT, B, H, SF, ST_FOUR_OVER_SIX>(a, grid, s);
         return hipErrorInvalidValue;
     case ST_BRUTE_FORCE:
         return launch_quant_t<InT, B, H, SF, ST_BRUTE_FORCE>(a, grid, s);
@@ -82,8 +82,12 @@ hipError_t dispatch_quant_st(const QuantArgs& a, int st, int grid, hipStream_t s
 
 template <class InT, int B, int H>
 hipError_t dispatch_quant_sf(const QuantArgs& a, int sf, int st, int grid, hipStream_t s) {
-    return sf == SF_E8M0 ? dispatch_quant_st<InT, B, H, SF_E8M0>(a, st, grid, s)
-                         : dispatch_quant_st<InT, B, H, SF_E4M3>(a, st, grid, s);
+    switch (sf) {
+    case SF_E8M0: return dispatch_quant_st<InT, B, H, SF_E8M0>(a, st, grid, s);
+    case SF_E4M3: return dispatch_quant_st<InT, B, H, SF_E4M3>(a, st, grid, s);
+    case SF_UE5M3: return dispatch_quant_st<InT, B, H, SF_UE5M3>(a, st, grid, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <class InT, int B>

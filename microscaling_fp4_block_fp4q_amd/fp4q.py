@@ -23,7 +23,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "fp4q.h")
 # enums (include/fp4q.h)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE = range(6)
 F32, BF16, F16 = 0, 1, 2
-E8M0, E4M3 = 0, 1
+E8M0, E4M3, UE5M3 = 0, 1, 2
 ABSMAX, PREVENT_ZERO, FOUR_OVER_SIX, BRUTE_FORCE, GIVEN = range(5)
 GLOBAL_NONE, GLOBAL_TENSOR_AMAX, GLOBAL_USER, GLOBAL_SEARCH = range(4)
 
