@@ -640,6 +640,23 @@ int oracle_block_mse(int fmt, int B, int H, const void* x, int x_dt, int64_t row
     return 0;
 }
 
+/* Codebook occupancy ([TORQ] section 2.B: the codeword usage whose collapse
+ * onto the smallest codes the method measures against the uniform
+ * distribution): counts[c] = number of nibbles equal to c, c = 0..15, in
+ * packed codes [rows, cols/2] (sign bit 3, E2M1 magnitude bits 0-2). */
+int oracle_code_histogram(const uint8_t* codes, int64_t rows, int64_t cols, uint64_t* counts)
+{
+    if (cols % 2) return -1;
+    for (int c = 0; c < 16; ++c) counts[c] = 0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j) {
+            uint8_t byte = codes[r * (cols / 2) + j / 2];
+            int q = (j & 1) ? (byte >> 4) : (byte & 15);
+            counts[q] += 1;
+        }
+    return 0;
+}
+
 /* FOCUS relaxed fake-quant forward ([FOCUS] methods 2-3): per sub-block k of
  * K values, S_q = fl(S_dq * c_k) with c_k an FP16 coefficient; the element
  * is encoded with u = fl(W / S_q) (0 when S_q is 0) and dequantized with the

@@ -72,6 +72,7 @@ def lib():
         L.oracle_tensor_global_scale.restype = f
         L.oracle_global_scale_search.argtypes = [i, i, i, p, i, i64, i64, i64, p]
         L.oracle_global_scale_search.restype = f
+        L.oracle_code_histogram.argtypes, L.oracle_code_histogram.restype = [p, i64, i64, p], i
         L.oracle_quantize.argtypes = [i, i, i, i, f, i, p, i, i64, i64, i64,
                                       p, p, p, p, i, i64, p, p]
         L.oracle_quantize.restype = i
@@ -231,6 +232,16 @@ def quantize(x: np.ndarray, *, fmt: int, block: int, strategy: int = ABSMAX,
     if rc != 0:
         raise ValueError("oracle_quantize rejected its arguments")
     return dict(codes=codes, scales=scales, g=np.float32(g[0]), dequant=dq, mse=mse, sse=sse)
+
+
+def code_histogram(codes: np.ndarray) -> np.ndarray:
+    """Counts of the 16 nibble codes in packed codes [rows, cols/2]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    counts = np.zeros(16, np.uint64)
+    if lib().oracle_code_histogram(_ptr(codes), rows, 2 * half, _ptr(counts)) != 0:
+        raise ValueError("oracle_code_histogram rejected its arguments")
+    return counts
 
 
 def dequantize(codes, scales, g, *, fmt, block, rows, cols, out_dt=DT_F32):
