@@ -314,6 +314,34 @@ def time_quantize_configs(F, torch, x, cfgs, reps=5):
     return out
 
 
+def time_histogram(F, torch, x, reps=10):
+    """Codebook-occupancy histogram (outside the step) of the NVFP4 codes of
+    one 4096 x 4096 input: HBM-bound over rows * cols / 2 code bytes."""
+    L = F.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    R, C = x.shape
+    codes = F.quantize(x, F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_NONE), want_mse=False)["codes"]
+    counts = torch.zeros(16, dtype=torch.int64, device=x.device)
+    ev = []
+    for _ in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st_ = L.fp4q_code_histogram(ctypes.c_void_p(codes.data_ptr()), R, C, ctypes.c_void_p(counts.data_ptr()),
+                                    stream)
+        e1.record()
+        if st_ != 0:
+            raise RuntimeError(f"histogram: status {st_}")
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev[1:]]))
+    h = counts.cpu().numpy() / (reps + 1)                 # the calls accumulate
+    return {"ms": round(ms, 4), "GB/s": round(R * C / 2 / (ms * 1e6), 1),
+            "zero_code_fraction": round(float(h[0] + h[8]) / (R * C), 4),
+            "what": "not part of the step: counts of the 16 nibble codes of the NVFP4 (block 16, no per-tensor "
+                    "scale) codes of the 4096x4096 N(0,1) input, 8 MiB of code bytes"}
+
+
 def cpu_baseline(O, S, host, rows_per_tensor):
     """The oracle (single thread) on the first rows of every tensor, over the
     same call list as one GPU step."""
@@ -492,6 +520,7 @@ def main():
         ("4-over-6", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_SEARCH))])
     ue5m3 = time_quantize_configs(F, torch, X["normal"], [
         (f"B={B} {STRATS[st]}", F.config(F.UE5M3, B, st)) for B in (16, 4) for st in (0, 2, 3)])
+    hist = time_histogram(F, torch, X["normal"])
     stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
     sb = sum(c.nbytes for c, _ in stream_quant)
     sms = sum(ms for _, ms in stream_quant)
@@ -526,6 +555,7 @@ def main():
                                                  "quantize call's algorithmic bytes"),
         "ue5m3_scales": dict(ue5m3, what="not part of the step: quantize of the 4096x4096 N(0,1) input with "
                                          "UE5M3 block scales (no per-tensor scale), every output"),
+        "code_histogram": hist,
         "copy_reference": {"GB/s": round(copy_gbs, 1), "hbm_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
                            "what": "device copy (read + write bytes) of the four 64 MiB inputs in rotation, "
                                    "the same access pattern as the quantize calls; per_strategy frac_of_copy "

@@ -216,6 +216,17 @@ fp4q_status fp4q_relaxed_fakequant_bwd(const fp4q_config* cfg, const void* w, in
                                        const void* grad_out, int g_dt, int64_t ld_g,
                                        float* grad_c, void* stream);
 
+/* Codebook occupancy of packed codes (TORQ page, section 2.B: the usage of
+ * the FP4 codewords, whose collapse onto the smallest codes the method
+ * measures against the uniform distribution).  counts [16] device uint64,
+ * ACCUMULATED: counts[c] += number of nibbles equal to c (sign bit 3, E2M1
+ * magnitude bits 0-2) in codes [rows, cols/2], dense; zero counts before
+ * the first call (several tensors can share one count).  cols must be even
+ * (FP4Q_ERR_SHAPE); codes 16-byte aligned, counts 8-byte aligned
+ * (FP4Q_ERR_ALIGNMENT); an empty tensor adds nothing. */
+fp4q_status fp4q_code_histogram(const uint8_t* codes, int64_t rows, int64_t cols, uint64_t* counts,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,8 @@
 #include <stdint.h>
 
 #include "fp4q.h"
+#include <algorithm>
+
 #include "fp4q_launch.hpp"
 
 using namespace fp4q_dev;
@@ -388,6 +390,21 @@ fp4q_status fp4q_relaxed_fakequant_bwd(const fp4q_config* cfg, const void* w, in
     a.grad_c = grad_c;
     return device_status(
         launch_relaxed_bwd(a, w_dt, cfg->block, sub_block, grid_for(a.units), (hipStream_t)stream));
+}
+
+fp4q_status fp4q_code_histogram(const uint8_t* codes, int64_t rows, int64_t cols, uint64_t* counts,
+                                void* stream) {
+    if (!counts || rows < 0 || cols < 0) return FP4Q_ERR_INVALID_ARG;
+    if ((uintptr_t)counts & 7u) return FP4Q_ERR_ALIGNMENT;
+    if (cols % 2 != 0) return FP4Q_ERR_SHAPE;
+    const int64_t nbytes = rows * (cols / 2);
+    if (nbytes > 0) FP4Q_TRY(check_buffer(codes));
+    // few workgroups, each walking many 16-byte chunks: every workgroup ends with one
+    // 64-bit atomic per code on the same 128 bytes, which serialise in the cache
+    const int64_t chunks = (nbytes + 15) / 16;
+    const int grid = (int)std::min<int64_t>(std::max<int64_t>((chunks + 2047) / 2048, 1), 256);
+    return device_status(launch_code_hist(codes, nbytes, reinterpret_cast<unsigned long long*>(counts), grid,
+                                          (hipStream_t)stream));
 }
 
 }  // extern "C"

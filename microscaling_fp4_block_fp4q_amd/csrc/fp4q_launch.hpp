@@ -23,6 +23,8 @@ hipError_t launch_tree_reduce_f64(const double* in, int64_t n, int64_t in_stride
 hipError_t launch_gsearch_pick(const double* totals, int64_t stride, const uint32_t* amax_partials, int n_partials,
                                float* g_dev, hipStream_t s);
 
+hipError_t launch_code_hist(const uint8_t* codes, int64_t nbytes, unsigned long long* counts, int grid,
+                            hipStream_t s);
 hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t s);
 hipError_t launch_write_g(float* g_dev, float g, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int B, int DU, int grid, hipStream_t s);

@@ -1,6 +1,7 @@
 // misc_kernels.hip -- launchers of the per-tensor abs-max pre-pass,
 // dequantize, block MSE and FOCUS relaxed forward / backward kernels; the
-// reduction and pick steps of the per-tensor scale search.
+// reduction and pick steps of the per-tensor scale search; the code
+// histogram.
 #include "fp4q_launch.hpp"
 
 namespace fp4q_dev {
@@ -68,6 +69,64 @@ hipError_t launch_gsearch_pick(const double* totals, int64_t stride, const uint3
                                float* g_dev, hipStream_t s) {
     hipLaunchKernelGGL(k_gsearch_pick, dim3(1), dim3(kThreads), 0, s, totals, stride, amax_partials, n_partials,
                        g_dev);
+    return hipGetLastError();
+}
+
+// Codebook occupancy (TORQ page, section 2.B: codeword usage): counts of the
+// 16 nibble codes, added to the caller's counts.  Each lane adds into its own
+// LDS bins (bin-major, so the lanes of a wave hit distinct banks), the
+// workgroup sums them, and one 64-bit atomic add per code and workgroup
+// reaches global memory.
+
+__device__ __forceinline__ void hist_word(uint32_t* h, uint32_t w) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) atomicAdd(&h[((w >> (4 * k)) & 15u) * kThreads], 1u);
+}
+
+__global__ __launch_bounds__(kThreads) void k_code_hist(const uint8_t* codes, int64_t nbytes,
+                                                        unsigned long long* counts) {
+    __shared__ uint32_t s_h[16 * kThreads];
+    __shared__ uint32_t s_part[kThreads];
+    for (int i = threadIdx.x; i < 16 * kThreads; i += kThreads) s_h[i] = 0u;
+    __syncthreads();
+    uint32_t* h = s_h + threadIdx.x;
+    const int64_t nvec = nbytes / 16;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const uint4* src = reinterpret_cast<const uint4*>(codes);
+    for (int64_t v = t0; v < nvec; v += stride) {
+        const uint4 w = src[v];
+        hist_word(h, w.x);
+        hist_word(h, w.y);
+        hist_word(h, w.z);
+        hist_word(h, w.w);
+    }
+    for (int64_t b = nvec * 16 + t0; b < nbytes; b += stride) {
+        const uint32_t byte = codes[b];
+        atomicAdd(&h[(byte & 15u) * kThreads], 1u);
+        atomicAdd(&h[(byte >> 4) * kThreads], 1u);
+    }
+    __syncthreads();
+    // thread t sums code t & 15 over lanes 16 (t >> 4) .. 16 (t >> 4) + 15
+    const int code = threadIdx.x & 15, seg = threadIdx.x >> 4;
+    uint32_t part = 0;
+#pragma unroll
+    for (int l = 0; l < 16; ++l) part += s_h[code * kThreads + seg * 16 + l];
+    s_part[threadIdx.x] = part;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        unsigned long long total = 0;
+        for (int sgm = 0; sgm < kThreads / 16; ++sgm) total += s_part[sgm * 16 + threadIdx.x];
+        if (total) atomicAdd(&counts[threadIdx.x], total);
+    }
+}
+
+hipError_t launch_code_hist(const uint8_t* codes, int64_t nbytes, unsigned long long* counts, int grid,
+                            hipStream_t s) {
+    if (nbytes > 0) {
+        const int cap = resident_workgroups<k_code_hist>();
+        hipLaunchKernelGGL(k_code_hist, dim3(grid < cap ? grid : cap), dim3(kThreads), 0, s, codes, nbytes, counts);
+    }
     return hipGetLastError();
 }
 

@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.fp4q_relaxed_fakequant_bwd.restype = ctypes.c_int
         L.fp4q_relaxed_fakequant_bwd.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, i32, p,
                                                  ctypes.c_int, i64, p, p]
+        L.fp4q_code_histogram.restype = ctypes.c_int
+        L.fp4q_code_histogram.argtypes = [p, i64, i64, p, p]
         _lib = L
     return _lib
 
@@ -206,6 +208,12 @@ def fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g
     _check(st, "fp4q_relaxed_fakequant_bwd")
 
 
+def fp4q_code_histogram(codes, counts, stream=None):
+    rows, half = codes.shape
+    st = lib().fp4q_code_histogram(_ptr(codes), rows, 2 * half, _ptr(counts), _stream(stream))
+    _check(st, "fp4q_code_histogram")
+
+
 # --------------------------------------------------------------------------
 # allocating wrappers
 # --------------------------------------------------------------------------
@@ -266,3 +274,10 @@ def relaxed_fakequant_bwd(w, scales, c, grad_out, cfg, sub_block=8, g=None, stre
     grad_c = torch.empty((rows, cols // sub_block), dtype=torch.float32, device=w.device)
     fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g, stream)
     return grad_c
+
+
+def code_histogram(codes, stream=None):
+    """Counts of the 16 nibble codes in packed codes [rows, cols/2] (int64 tensor of 16)."""
+    counts = torch.zeros(16, dtype=torch.int64, device=codes.device)
+    fp4q_code_histogram(codes, counts, stream)
+    return counts

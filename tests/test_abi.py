@@ -105,6 +105,18 @@ def test_quantize_validation():
 
 @needs_lib
 @cpu_only
+def test_histogram_validation():
+    L = F.lib()
+    assert L.fp4q_code_histogram(P(A), 4, 64, None, None) == F.ERR_INVALID_ARG
+    assert L.fp4q_code_histogram(None, 4, 64, P(A), None) == F.ERR_INVALID_ARG
+    assert L.fp4q_code_histogram(P(A), -1, 64, P(A), None) == F.ERR_INVALID_ARG
+    assert L.fp4q_code_histogram(P(A), 4, 63, P(A), None) == F.ERR_SHAPE
+    assert L.fp4q_code_histogram(P(A + 4), 4, 64, P(A), None) == F.ERR_ALIGNMENT
+    assert L.fp4q_code_histogram(P(A), 4, 64, P(A + 4), None) == F.ERR_ALIGNMENT
+
+
+@needs_lib
+@cpu_only
 def test_other_entry_points_validation():
     L = F.lib()
     nv, mx = F.nvfp4(), F.mxfp4()
