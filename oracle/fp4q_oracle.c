@@ -657,6 +657,34 @@ int oracle_code_histogram(const uint8_t* codes, int64_t rows, int64_t cols, uint
     return 0;
 }
 
+/* FP4 GEMM on MXFP4 operands ([MR-GPTQ] section 2.3: the QuTLASS kernels
+ * multiply the packed FP4 weights and activations with their block scales):
+ * C[m][n] = sum over k of dq(A)[m][k] * dq(B)[n][k], with dq the MXFP4 decode
+ * (E2M1 grid value times 2^(scale-127) of the 32-element block, NaN for
+ * scale 0xFF).  A codes [M, K/2] + scales [M, K/32], B likewise [N, ...];
+ * products and sum in fp64 (every product of two decoded values is exact in
+ * fp64, so C is the exact dot product rounded once per addition). */
+int oracle_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                      const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, double* c)
+{
+    if (K % 32) return -1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                uint8_t ab = a_codes[m * (K / 2) + k / 2], bb = b_codes[n * (K / 2) + k / 2];
+                int qa = (k & 1) ? (ab >> 4) : (ab & 15), qb = (k & 1) ? (bb >> 4) : (bb & 15);
+                double sa = oracle_e8m0_decode(a_scales[m * (K / 32) + k / 32]);
+                double sb = oracle_e8m0_decode(b_scales[n * (K / 32) + k / 32]);
+                double va = ((qa & 8) ? -1.0 : 1.0) * E2M1_MAG[qa & 7] * sa;
+                double vb = ((qb & 8) ? -1.0 : 1.0) * E2M1_MAG[qb & 7] * sb;
+                acc += va * vb;
+            }
+            c[m * N + n] = acc;
+        }
+    return 0;
+}
+
 /* FOCUS relaxed fake-quant forward ([FOCUS] methods 2-3): per sub-block k of
  * K values, S_q = fl(S_dq * c_k) with c_k an FP16 coefficient; the element
  * is encoded with u = fl(W / S_q) (0 when S_q is 0) and dequantized with the

@@ -73,6 +73,7 @@ def lib():
         L.oracle_global_scale_search.argtypes = [i, i, i, p, i, i64, i64, i64, p]
         L.oracle_global_scale_search.restype = f
         L.oracle_code_histogram.argtypes, L.oracle_code_histogram.restype = [p, i64, i64, p], i
+        L.oracle_mxfp4_gemm.argtypes, L.oracle_mxfp4_gemm.restype = [p, p, p, p, i64, i64, i64, p], i
         L.oracle_quantize.argtypes = [i, i, i, i, f, i, p, i, i64, i64, i64,
                                       p, p, p, p, i, i64, p, p]
         L.oracle_quantize.restype = i
@@ -242,6 +243,17 @@ def code_histogram(codes: np.ndarray) -> np.ndarray:
     if lib().oracle_code_histogram(_ptr(codes), rows, 2 * half, _ptr(counts)) != 0:
         raise ValueError("oracle_code_histogram rejected its arguments")
     return counts
+
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales) -> np.ndarray:
+    """C = dq(A) dq(B)^T in fp64 for MXFP4 operands (codes [rows, K/2], E8M0 scales [rows, K/32])."""
+    a_codes, b_codes = (np.ascontiguousarray(t, dtype=np.uint8) for t in (a_codes, b_codes))
+    a_scales, b_scales = (np.ascontiguousarray(t, dtype=np.uint8) for t in (a_scales, b_scales))
+    M, N, K = a_codes.shape[0], b_codes.shape[0], 2 * a_codes.shape[1]
+    c = np.zeros((M, N), np.float64)
+    if lib().oracle_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K, _ptr(c)) != 0:
+        raise ValueError("oracle_mxfp4_gemm rejected its arguments")
+    return c
 
 
 def dequantize(codes, scales, g, *, fmt, block, rows, cols, out_dt=DT_F32):

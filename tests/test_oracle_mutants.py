@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "fp4q_oracle.c")
 PIN_FILES = ["test_oracle_formats.py", "test_oracle_quant.py", "test_oracle_golden.py",
              "test_oracle_rotation.py", "test_oracle_focus.py", "test_oracle_search.py",
-             "test_oracle_ue5m3.py", "test_oracle_histogram.py"]
+             "test_oracle_ue5m3.py", "test_oracle_histogram.py", "test_oracle_gemm.py"]
 
 # (name, text in the oracle, replacement, which occurrence (1-based))
 MUTANTS = [
@@ -79,6 +79,9 @@ MUTANTS = [
     ("focus clip bound exclusive", "inside = fabsf(u) <= 6.0f;", "inside = fabsf(u) < 6.0f;", 1),
     ("focus gradient over c not c^2", "float cc = c_k * c_k;", "float cc = c_k;", 1),
     ("histogram drops the sign bit", "counts[q] += 1;", "counts[q & 7] += 1;", 1),
+    ("gemm reads A's nibbles swapped", "int qa = (k & 1) ? (ab >> 4) : (ab & 15),",
+     "int qa = (k & 1) ? (ab & 15) : (ab >> 4),", 1),
+    ("gemm ignores B's scale", "double sb = oracle_e8m0_decode(b_scales[n * (K / 32) + k / 32]);", "double sb = 1.0;", 1),
     ("search ties to the larger shrink", "if (j == 0 || total < best_total ||", "if (j == 0 || total <= best_total ||", 1),
     ("search candidate step 1/32", "float g = g0 * (float)(1.0 - j / 64.0);", "float g = g0 * (float)(1.0 - j / 32.0);", 1),
     ("search result ignores the winner", "return g0 * (float)(1.0 - best / 64.0);", "return g0;", 1),
