@@ -227,6 +227,21 @@ fp4q_status fp4q_relaxed_fakequant_bwd(const fp4q_config* cfg, const void* w, in
 fp4q_status fp4q_code_histogram(const uint8_t* codes, int64_t rows, int64_t cols, uint64_t* counts,
                                 void* stream);
 
+/* FP4 GEMM on MXFP4 operands (the FP4 matrix products of the MR-GPTQ page,
+ * section 2.3, run on gfx950's block-scaled matrix cores):
+ *   C[m][n] = sum_k dq(A)[m][k] * dq(B)[n][k]
+ * with dq the MXFP4 decode (E2M1 value times 2^(scale-127) of its 32-element
+ * block).  A codes [M, K/2] + E8M0 scales [M, K/32] and B codes [N, K/2] +
+ * scales [N, K/32], dense: the layouts fp4q_quantize writes for {E8M0, 32}
+ * (B is the [out, in] weight, A the [tokens, in] activation).  C [M, ldc] of
+ * type c_dt (FP4Q_F32 or FP4Q_BF16, rounded half-to-even), ldc >= N.
+ * Accumulation is fp32 inside the matrix cores.  K must be a multiple of 128
+ * (FP4Q_ERR_SHAPE); codes and C 16-byte aligned, ldc * element size a
+ * multiple of 16, scales 4-byte aligned (FP4Q_ERR_ALIGNMENT). */
+fp4q_status fp4q_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                            const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, int c_dt,
+                            int64_t ldc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

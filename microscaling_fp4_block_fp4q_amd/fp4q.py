@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_int, i64, p, p]
         L.fp4q_code_histogram.restype = ctypes.c_int
         L.fp4q_code_histogram.argtypes = [p, i64, i64, p, p]
+        L.fp4q_mxfp4_gemm.restype = ctypes.c_int
+        L.fp4q_mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, ctypes.c_int, i64, p]
         _lib = L
     return _lib
 
@@ -214,6 +216,14 @@ def fp4q_code_histogram(codes, counts, stream=None):
     _check(st, "fp4q_code_histogram")
 
 
+def fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, stream=None):
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    K = 2 * a_codes.shape[1]
+    st = lib().fp4q_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K, _ptr(c),
+                               dtype_code(c), c.stride(0), _stream(stream))
+    _check(st, "fp4q_mxfp4_gemm")
+
+
 # --------------------------------------------------------------------------
 # allocating wrappers
 # --------------------------------------------------------------------------
@@ -281,3 +291,10 @@ def code_histogram(codes, stream=None):
     counts = torch.zeros(16, dtype=torch.int64, device=codes.device)
     fp4q_code_histogram(codes, counts, stream)
     return counts
+
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.float32, stream=None):
+    """C [M, N] = dq(A) dq(B)^T for MXFP4 operands (codes [rows, K/2], E8M0 scales [rows, K/32])."""
+    c = torch.empty((a_codes.shape[0], b_codes.shape[0]), dtype=out_dtype, device=a_codes.device)
+    fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, stream)
+    return c

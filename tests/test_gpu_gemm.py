@@ -1,0 +1,102 @@
+"""GPU parity of the MXFP4 GEMM (block-scaled matrix cores) against the
+oracle's fp64 product C = dq(A) dq(B)^T.
+
+Tolerance, from the arithmetic: every product of two decoded MXFP4 values
+is exact in fp32 (at most 2 x 2 significant bits times a power of two), the
+matrix core adds the 128 products of one instruction and the running sum,
+and the running fp32 sum is rounded once per 128-long K step.  So
+|C_gpu - C| <= (K/128 + 1) * 2^-24 * sum_k |a_k b_k|; the test allows twice
+that.  bf16 output adds the final rounding (2^-8 relative)."""
+import numpy as np
+import pytest
+import torch
+
+from microscaling_fp4_block_fp4q_amd import fp4q as F
+from microscaling_fp4_block_fp4q_amd import synth as S
+from oracle import oracle as O
+
+from gpu_helpers import DEV, note
+
+pytestmark = pytest.mark.gpu
+
+
+def operands(seed, M, N, K, spread=4):
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 256, (M, K // 2)).astype(np.uint8)
+    b = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    sa = (127 + rng.integers(-spread, spread + 1, (M, K // 32))).astype(np.uint8)
+    sb = (127 + rng.integers(-spread, spread + 1, (N, K // 32))).astype(np.uint8)
+    return a, sa, b, sb
+
+
+def abs_product(a, sa, b, sb):
+    K = a.shape[1] * 2
+    A = O.dequantize(a, sa, 1.0, fmt=0, block=32, rows=a.shape[0], cols=K).astype(np.float64)
+    B = O.dequantize(b, sb, 1.0, fmt=0, block=32, rows=b.shape[0], cols=K).astype(np.float64)
+    return np.abs(A) @ np.abs(B).T
+
+
+def run_gpu(a, sa, b, sb, out=torch.float32):
+    t = [torch.from_numpy(v).to(DEV) for v in (a, sa, b, sb)]
+    c = F.mxfp4_gemm(*t, out_dtype=out)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy().astype(np.float64)
+
+
+def check(got, want, bound_abs, K, bf16=False):
+    tol = 2 * (K / 128 + 1) * 2.0 ** -24 * bound_abs
+    if bf16:
+        tol = tol + 2.0 ** -8 * np.abs(want)
+    bad = np.abs(got - want) > tol
+    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:3].tolist())
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (256, 256, 1024), (512, 768, 512), (96, 200, 256),
+                                   (16, 16, 128), (300, 1000, 384)])
+def test_random_codes(O_lib, M, N, K):
+    a, sa, b, sb = operands(M + N + K, M, N, K)
+    note(f"gemm random {M}x{N}x{K}")
+    got = run_gpu(a, sa, b, sb)
+    want = O.mxfp4_gemm(a, sa, b, sb)
+    check(got, want, abs_product(a, sa, b, sb), K)
+
+
+def test_bf16_output(O_lib):
+    a, sa, b, sb = operands(5, 256, 512, 256)
+    note("gemm bf16 output")
+    got = run_gpu(a, sa, b, sb, torch.bfloat16)
+    want = O.mxfp4_gemm(a, sa, b, sb)
+    check(got, want, abs_product(a, sa, b, sb), 256, bf16=True)
+
+
+def test_quantized_llm_shapes(O_lib):
+    """Activations [tokens, hidden] times an MLP weight [out, in], both
+    quantized to MXFP4 by the library; the oracle's product on sampled rows."""
+    x = S.laplace(512, 4096, 5)
+    w = S.normal(1024, 4096, 6) * np.float32(0.02)
+    note("gemm of library-quantized 512x4096 and 1024x4096")
+    qa = F.quantize(S.to_torch(x, S.F32, DEV), F.mxfp4(), want_mse=False)
+    qb = F.quantize(S.to_torch(w.astype(np.float32), S.F32, DEV), F.mxfp4(), want_mse=False)
+    c = F.mxfp4_gemm(qa["codes"], qa["scales"], qb["codes"], qb["scales"])
+    torch.cuda.synchronize()
+    a, sa = qa["codes"].cpu().numpy(), qa["scales"].cpu().numpy()
+    b, sb = qb["codes"].cpu().numpy(), qb["scales"].cpu().numpy()
+    rows = np.array([0, 1, 255, 511])
+    want = O.mxfp4_gemm(a[rows], sa[rows], b, sb)
+    check(c.cpu().numpy().astype(np.float64)[rows], want, abs_product(a[rows], sa[rows], b, sb), 4096)
+
+
+def test_wide_scale_range(O_lib):
+    a, sa, b, sb = operands(9, 256, 256, 512, spread=40)
+    note("gemm wide scale range")
+    check(run_gpu(a, sa, b, sb), O.mxfp4_gemm(a, sa, b, sb), abs_product(a, sa, b, sb), 512)
+
+
+def test_empty_and_validation(O_lib):
+    L = F.lib()
+    z = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    c = torch.zeros((4, 4), dtype=torch.float32, device=DEV)
+    p = lambda t: t.data_ptr()
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 0, 4, 128, p(c), F.F32, 4, None) == F.OK
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 100, p(c), F.F32, 4, None) == F.ERR_SHAPE
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 128, p(c), F.F16, 4, None) == F.ERR_INVALID_ARG
