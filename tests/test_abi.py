@@ -10,6 +10,8 @@ GPU device node exists.
 import ctypes
 import os
 
+import re
+
 import pytest
 
 from microscaling_fp4_block_fp4q_amd import fp4q as F
@@ -36,7 +38,9 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_version_strings_workspace():
-    assert F.abi_version() == 2
+    hdr = open(F.HEADER).read()
+    declared = int(re.search(r"#define FP4Q_ABI_VERSION (\d+)", hdr).group(1))
+    assert F.abi_version() == declared == F.ABI_VERSION
     for s in range(6):
         assert F.status_string(s) and F.status_string(s) != "unknown status"
     assert F.status_string(99) == "unknown status"
