@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 2
+#define FP4Q_ABI_VERSION 3
 
 typedef enum {
     FP4Q_OK = 0,
@@ -235,12 +235,18 @@ fp4q_status fp4q_code_histogram(const uint8_t* codes, int64_t rows, int64_t cols
  * scales [N, K/32], dense: the layouts fp4q_quantize writes for {E8M0, 32}
  * (B is the [out, in] weight, A the [tokens, in] activation).  C [M, ldc] of
  * type c_dt (FP4Q_F32 or FP4Q_BF16, rounded half-to-even), ldc >= N.
- * Accumulation is fp32 inside the matrix cores.  K must be a multiple of 128
- * (FP4Q_ERR_SHAPE); codes and C 16-byte aligned, ldc * element size a
- * multiple of 16, scales 4-byte aligned (FP4Q_ERR_ALIGNMENT). */
+ * Accumulation is fp32 inside the matrix cores, in an order of its own.
+ * workspace: fp4q_mxfp4_gemm_workspace_bytes(M, N, K) bytes of device
+ * memory, 256-byte aligned, owned by the caller (the scales rearranged for
+ * the matrix cores go there; its contents need no initialisation and are
+ * dead after the call).  K must be a positive multiple of 256 and M * K / 2,
+ * N * K / 2 below 2^32 (FP4Q_ERR_SHAPE); codes and C 16-byte aligned,
+ * ldc * element size a multiple of 16, scales 4-byte aligned, workspace
+ * 256-byte aligned (FP4Q_ERR_ALIGNMENT). */
+size_t fp4q_mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 fp4q_status fp4q_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                             const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, int c_dt,
-                            int64_t ldc, void* stream);
+                            int64_t ldc, void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

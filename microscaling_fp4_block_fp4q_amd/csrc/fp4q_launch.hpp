@@ -23,8 +23,9 @@ hipError_t launch_tree_reduce_f64(const double* in, int64_t n, int64_t in_stride
 hipError_t launch_gsearch_pick(const double* totals, int64_t stride, const uint32_t* amax_partials, int n_partials,
                                float* g_dev, hipStream_t s);
 
+size_t mxfp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mxfp4_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
-                             int64_t N, int64_t K, void* c, int c_dt, int64_t ldc, hipStream_t s);
+                             int64_t N, int64_t K, void* c, int c_dt, int64_t ldc, void* workspace, hipStream_t s);
 hipError_t launch_code_hist(const uint8_t* codes, int64_t nbytes, unsigned long long* counts, int grid,
                             hipStream_t s);
 hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t s);

@@ -3,49 +3,88 @@
 // QuTLASS kernels run on Blackwell; here on CDNA4 matrix cores).
 //
 // C[M, N] = dq(A) dq(B)^T with A codes [M, K/2] + E8M0 scales [M, K/32] and
-// B codes [N, K/2] + scales [N, K/32]: exactly the layouts fp4q_quantize
-// writes for {E8M0, block 32}.  v_mfma_scale_f32_16x16x128_f8f6f4 with both
-// operands in E2M1 multiplies a 16 x 128 A fragment by a 16 x 128 B fragment
-// and applies one E8M0 scale per operand lane: lane l holds row l % 16 and the
-// 32 consecutive K values of block l / 16, which is the 16 contiguous code
-// bytes of that row and block, and its block's scale byte.  The result lane l
-// holds column l % 16 of rows 4 (l / 16) .. 4 (l / 16) + 3.
+// B codes [N, K/2] + scales [N, K/32]: the layouts fp4q_quantize writes for
+// {E8M0, block 32}.
+//
+// Matrix core: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in E2M1
+// (on gfx950 this shape runs E2M1 at twice the E4M3 rate; 16 x 16 x 128 runs
+// both at the E4M3 rate).  Operand lane l holds row l % 32 of a 32-row
+// fragment and the 32 K values of K block l / 32 of the 64-wide K substep (16
+// code bytes), and a scale dword whose byte op_sel is that block's scale.
+// The result lane l holds column l % 32 of the second operand's rows and
+// rows 8 (r / 4) + 4 (l / 32) + r % 4 of the first's.  B goes first, so a
+// lane ends up with one row of C and 4 consecutive columns per r / 4.
 //
 // Tiling: a workgroup of 4 waves computes a 256 x 256 tile of C, each wave a
-// 128 x 128 quarter (8 x 8 MFMA fragments, 256 fp32 accumulators per lane,
-// which the compiler keeps in the accumulation registers).  K advances 128
-// at a time; each K slice (256 rows x 64 code bytes of A and of B, and their
-// scale words) goes straight from global memory into LDS with the direct
-// loads, 4 slices deep, so three slices are loading while the MFMAs consume
-// the fourth.  In LDS the fragments lie in the order the MFMA lanes read
-// them, so every fragment read is one linear, conflict-free 1 KB read.
+// 128 x 128 quarter (4 x 4 fragments, 256 fp32 accumulators per lane in the
+// accumulation registers).  K advances 256 per step.  A step's codes (256
+// rows x 128 bytes of A and of B) go straight from global memory into one of
+// two LDS stages with the direct loads, each load reading 8 whole 128-byte
+// rows; the next step's load runs while the current step computes.  Within a
+// row the eight 16-byte chunks are stored XOR-swizzled by the row, so both
+// the direct-load writes and the fragment reads are free of bank conflicts.
+//
+// Scales: a small pass first rewrites each operand's [rows, K/32] scale bytes
+// into the per-lane dwords the MFMA takes (for fragment f, step t, lane l:
+// the scales of K blocks 8 t + 2 h + l / 32 of row 32 f + l % 32, h = 0..3),
+// so each step's scales are one coalesced 256-byte load per fragment.
+//
+// Epilogue: the accumulators go through LDS (per wave, a 32-row block at a
+// time) and leave as 16-byte stores of whole row pieces.
 #include "fp4q_launch.hpp"
 
 namespace fp4q_dev {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-constexpr int kGemmTileM = 256;
-constexpr int kGemmTileN = 256;
-constexpr int kGemmK = 128;                      // K per step: 4 scale blocks
-constexpr int kGemmRowBytes = kGemmK / 2;        // code bytes of one row per step
+constexpr int kGemmTile = 256;                   // tile rows of A and of B
+constexpr int kGemmStepK = 256;                  // K per step: 8 scale blocks
+constexpr int kGemmRowBytes = kGemmStepK / 2;    // code bytes of a row per step
+constexpr int kGemmOperandBytes = kGemmTile * kGemmRowBytes;   // 32 KB
+constexpr int kGemmDmaPerOperand = kGemmOperandBytes / 1024 / 4;  // direct loads per wave
+// Vector-memory operations a wave issues per step: the direct loads of A and
+// B and the 8 scale-dword loads (4 A fragments, 4 B fragments).
+constexpr int kGemmLoadsPerStep = 2 * kGemmDmaPerOperand + 8;
 
 struct GemmArgs {
     const uint8_t* a;
-    const uint8_t* as;
     const uint8_t* b;
-    const uint8_t* bs;
+    const uint32_t* sa;                          // shuffled scale dwords
+    const uint32_t* sb;
     int64_t M, N, K;
     void* c;
     int c_dt;
     int64_t ldc;
     int tiles_m, tiles_n;
+    int steps;                                   // K / 256
+    int frags_a, frags_b;                        // ceil(M / 32), ceil(N / 32)
 };
 
-__device__ __forceinline__ v8i frag_of(const uint4 v) {
-    v8i f = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-    return f;
+// ---------------------------------------------------------------------------
+// Scale shuffle: out[(f * T + t) * 64 + l] = scale bytes of K blocks
+// 8 t + l / 32 + {0, 2, 4, 6} of row 32 f + l % 32 (byte h = block
+// 8 t + 2 h + l / 32); rows past the matrix get 127 (2^0).
+// ---------------------------------------------------------------------------
+__global__ void k_gemm_shuffle_scales(const uint8_t* __restrict__ s, int64_t rows, int64_t kblocks, int steps,
+                                      int64_t total, uint32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int l = (int)(i & 63);
+    const int64_t ft = i >> 6;
+    const int t = (int)(ft % steps);
+    const int64_t row = (ft / steps) * 32 + (l & 31);
+    uint32_t w = 0x7F7F7F7Fu;
+    if (row < rows) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(s + row * kblocks + 8 * t);
+        const uint32_t lo = p[0], hi = p[1];     // blocks 8 t .. 8 t + 7
+        // bytes l / 32 and 2 + l / 32 of lo, then of hi
+        w = __builtin_amdgcn_perm(hi, lo, (l >> 5) ? 0x07050301u : 0x06040200u);
+    }
+    out[i] = w;
 }
 
 // Tile order: workgroups go round-robin to the 8 XCDs (blockIdx % 8), each
@@ -66,177 +105,288 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, int& tm, int& tn) {
     tn = (t % in_group) / gsize;
 }
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-constexpr int kGemmStages = 4;                   // K slices in flight
-constexpr int kFragBytes = 64 * 16;              // one MFMA operand fragment
-constexpr int kSliceBytes = 16 * kFragBytes;     // 256 rows x 64 code bytes
-// Direct global -> LDS loads each wave issues per slice: 4 A fragments,
-// 4 B fragments, one A-scale and one B-scale dword per lane.
-constexpr int kDmaPerSlice = 10;
-
-// Wait until at most n of this wave's direct loads are outstanding (the
-// compiler's own waits would wait for all of them), then a workgroup barrier
-// without the fence of __syncthreads (the fence would also drain them).
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// and all its LDS reads have completed, then a workgroup barrier, fenced for
+// the compiler only: __syncthreads' fence would also wait for every load.
+// The compiler does not know that the barrier is what makes the other waves'
+// direct loads visible, so the empty asm statements keep it from moving
+// memory accesses across.
 template <int N>
 __device__ __forceinline__ void gemm_wait_barrier() {
     static_assert(N < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-// Issue the direct loads of K slice ks into LDS stage buffers.  LDS holds
-// fragments in the order the MFMA reads them: fragment f (rows 16 f .. 16 f
-// + 15 of the slice) at f * 1024, lane l's 16 bytes (row 16 f + l % 16, K
-// block l / 16) at + 16 l, so a fragment read is one linear 1 KB ds_read.
-// Scales: row-major words (the 4 K-block scale bytes of a row).  Rows past
-// the matrix read its last row; their results are not stored.
-__device__ __forceinline__ void gemm_issue(const GemmArgs& p, int64_t m0, int64_t n0, int ks, uint8_t* sa,
-                                           uint8_t* sb, uint32_t* ssa, uint32_t* ssb, int wave, int lane) {
-    const int64_t kbytes = p.K / 2, kscales = p.K / 32;
-    const int64_t koff = (int64_t)ks * kGemmRowBytes + (lane >> 4) * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int f = wave * 4 + q;
-        const int r = 16 * f + (lane & 15);
-        const int64_t ra = min<int64_t>(m0 + r, p.M - 1), rb = min<int64_t>(n0 + r, p.N - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(p.a + ra * kbytes + koff), (lds_void_ptr)(sa + f * kFragBytes),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(p.b + rb * kbytes + koff), (lds_void_ptr)(sb + f * kFragBytes),
-                                         16, 0, 0);
-    }
-    const int r = wave * 64 + lane;
-    const int64_t ra = min<int64_t>(m0 + r, p.M - 1), rb = min<int64_t>(n0 + r, p.N - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(p.as + ra * kscales + (int64_t)ks * 4),
-                                     (lds_void_ptr)(ssa + wave * 64), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(p.bs + rb * kscales + (int64_t)ks * 4),
-                                     (lds_void_ptr)(ssb + wave * 64), 4, 0, 0);
-}
-
-// One K slice in LDS.  Four of them, as four separate objects: the compiler
-// tracks the direct loads per LDS object, so reading one stage does not make
-// it wait for the loads still filling the others.
-struct GemmSlice {
-    uint8_t a[kSliceBytes];
-    uint8_t b[kSliceBytes];
-    uint32_t as[kGemmTileM];
-    uint32_t bs[kGemmTileN];
+// One step's codes.  Two stages, as two separate objects: the compiler tracks
+// the direct loads per LDS object, so reading one stage does not make it wait
+// for the loads still filling the other.  Row r's chunk c (16 bytes, K block
+// c of the step) sits at r * 128 + 16 (c ^ (r % 8)).
+struct GemmStage {
+    uint8_t a[kGemmOperandBytes];
+    uint8_t b[kGemmOperandBytes];
 };
-__shared__ __attribute__((aligned(1024))) GemmSlice g_slice0;
-__shared__ __attribute__((aligned(1024))) GemmSlice g_slice1;
-__shared__ __attribute__((aligned(1024))) GemmSlice g_slice2;
-__shared__ __attribute__((aligned(1024))) GemmSlice g_slice3;
+__shared__ __attribute__((aligned(1024))) GemmStage g_stage0;
+__shared__ __attribute__((aligned(1024))) GemmStage g_stage1;
 
 template <int S>
-__device__ __forceinline__ GemmSlice& gemm_slice() {
-    if constexpr (S == 0) return g_slice0;
-    else if constexpr (S == 1) return g_slice1;
-    else if constexpr (S == 2) return g_slice2;
-    else return g_slice3;
+__device__ __forceinline__ GemmStage& gemm_stage() {
+    if constexpr (S == 0) return g_stage0;
+    else return g_stage1;
 }
 
-template <int S>
-__device__ __forceinline__ void gemm_issue_slice(const GemmArgs& p, int64_t m0, int64_t n0, int ks, int wave,
-                                                 int lane) {
-    GemmSlice& sl = gemm_slice<S>();
-    gemm_issue(p, m0, n0, ks, sl.a, sl.b, sl.as, sl.bs, wave, lane);
-}
+// Per-lane state fixed for the whole K loop.
+struct GemmLane {
+    uint32_t oa[kGemmDmaPerOperand], ob[kGemmDmaPerOperand];   // direct-load byte offsets
+    const uint32_t* sa;                          // scale dwords of this wave's first A fragment, step 0
+    const uint32_t* sb;
+};
 
-// One K step on stage S (slice ks): wait for it, refill the stage the
-// previous step used with slice ks + 3, and run the 64 MFMAs of this wave.
-// The refill is issued on every step, also past the last slice (it then
-// reloads the last slice into a stage nobody reads again): with the direct
-// loads outside any branch, the compiler knows which stage each pending load
-// fills and adds no wait of its own before the fragment reads.
-template <int S>
-__device__ __forceinline__ void gemm_step(const GemmArgs& p, int64_t m0, int64_t n0, int ks, int nk, int wave,
-                                          int lane, int wm, int wn, v4f (&acc)[8][8]) {
-    gemm_wait_barrier<2 * kDmaPerSlice>();
-    gemm_issue_slice<(S + kGemmStages - 1) % kGemmStages>(p, m0, n0, min(ks + kGemmStages - 1, nk - 1), wave, lane);
-    if (ks >= nk) return;
-    const GemmSlice& sl = gemm_slice<S>();
-    const int fr = lane & 15, kb = lane >> 4;    // fragment row and K block of this lane
-    v8i bf[8];
-    int bsc[8];
+// Direct load q of wave w covers tile rows 8 (8 w + q) .. + 7, 1 KB of LDS:
+// lane l writes 16 bytes at + 16 l, i.e. row 8 (8 w + q) + l / 8, slot l % 8,
+// which holds chunk (l % 8) ^ (row % 8) - the 8 lanes of a row read its whole
+// 128 bytes.  Rows past the matrix read its last row (results not stored).
+__device__ __forceinline__ GemmLane gemm_lane(const GemmArgs& p, int64_t m0, int64_t n0, int wave, int lane,
+                                              int wm, int wn) {
+    const int64_t kbytes = p.K / 2;
+    const int sub = lane >> 3, chunk = (lane & 7) ^ (sub & 7);
+    GemmLane L;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int f = wn * 8 + j;
-        bf[j] = frag_of(*reinterpret_cast<const uint4*>(&sl.b[f * kFragBytes + lane * 16]));
-        bsc[j] = (int)((sl.bs[16 * f + fr] >> (8 * kb)) & 0xFFu);
+    for (int q = 0; q < kGemmDmaPerOperand; ++q) {
+        const int r = 8 * (kGemmDmaPerOperand * wave + q) + sub;
+        L.oa[q] = (uint32_t)(min<int64_t>(m0 + r, p.M - 1) * kbytes + 16 * chunk);
+        L.ob[q] = (uint32_t)(min<int64_t>(n0 + r, p.N - 1) * kbytes + 16 * chunk);
+    }
+    L.sa = p.sa + (int64_t)((m0 + 128 * wm) / 32) * p.steps * 64 + lane;
+    L.sb = p.sb + (int64_t)((n0 + 128 * wn) / 32) * p.steps * 64 + lane;
+    return L;
+}
+
+// The 8 scale dwords of one step for this wave: 4 A fragments, 4 B
+// fragments (fragments past the matrix take its last one).
+struct GemmScales {
+    int a[4], b[4];
+};
+
+// Issue step t's loads: the codes into stage S, the scale dwords into sc.
+template <int S>
+__device__ __forceinline__ void gemm_issue(const GemmArgs& p, const GemmLane& L, int t, int wave, int64_t fa0,
+                                           int64_t fb0, GemmScales& sc) {
+    GemmStage& st = gemm_stage<S>();
+    const uint8_t* a = p.a + (int64_t)t * kGemmRowBytes;
+    const uint8_t* b = p.b + (int64_t)t * kGemmRowBytes;
+#pragma unroll
+    for (int q = 0; q < kGemmDmaPerOperand; ++q) {
+        const int j = kGemmDmaPerOperand * wave + q;
+        __builtin_amdgcn_global_load_lds((const void*)(a + L.oa[q]), (lds_void_ptr)(st.a + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(b + L.ob[q]), (lds_void_ptr)(st.b + j * 1024), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int f = wm * 8 + i;
-        const v8i af = frag_of(*reinterpret_cast<const uint4*>(&sl.a[f * kFragBytes + lane * 16]));
-        const int asc = (int)((sl.as[16 * f + fr] >> (8 * kb)) & 0xFFu);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 4, 4, 0, asc, 0, bsc[j]);
+    for (int i = 0; i < 4; ++i) {
+        const int64_t fa = min<int64_t>(fa0 + i, p.frags_a - 1) - fa0;
+        const int64_t fb = min<int64_t>(fb0 + i, p.frags_b - 1) - fb0;
+        sc.a[i] = (int)L.sa[(fa * p.steps + t) * 64];
+        sc.b[i] = (int)L.sb[(fb * p.steps + t) * 64];
     }
 }
 
+// One 16-byte fragment read from LDS as a single vector load, widened to the
+// 8-dword operand (E2M1 uses the low 4 dwords).
+__device__ __forceinline__ v8i frag_at(const uint8_t* p) {
+    const v4i v = *reinterpret_cast<const v4i*>(p);
+    v8i f = {v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+    return f;
+}
+
+// Fragments of one K substep h: A rows 128 wm + 32 i + l % 32, B rows
+// 128 wn + 32 j + l % 32, chunk 2 h + l / 32.
+struct GemmFrags {
+    v8i a[4], b[4];
+};
+
+template <int S>
+__device__ __forceinline__ void gemm_read(GemmFrags& fr, int h, int lane, int wm, int wn) {
+    const GemmStage& st = gemm_stage<S>();
+    const int r = lane & 31;
+    const int slot = (2 * h + (lane >> 5)) ^ (r & 7);
+    const int off = r * kGemmRowBytes + 16 * slot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fr.a[i] = frag_at(st.a + ((128 * wm + 32 * i) * kGemmRowBytes + off));
+        fr.b[i] = frag_at(st.b + ((128 * wn + 32 * i) * kGemmRowBytes + off));
+    }
+}
+
+template <int H>
+__device__ __forceinline__ void gemm_mfma(const GemmFrags& fr, const GemmScales& sc, v16f (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr.b[j], fr.a[i], acc[i][j], 4, 4, H,
+                                                                        sc.b[j], H, sc.a[i]);
+}
+
+// Step t on stage S with scales sc: the four K substeps, each substep's
+// fragments read while the previous substep's MFMAs run.  Then wait for step
+// t + 1's loads, pass the barrier (every wave is done with stage S) and refill
+// stage S and sc with step t + 2 (re-reading the last step past the end, so
+// the direct loads stay outside any branch and the compiler adds no wait of
+// its own before the fragment reads).
+template <int S>
+__device__ __forceinline__ void gemm_step(const GemmArgs& p, const GemmLane& L, int t, int wave, int lane, int wm,
+                                          int wn, int64_t fa0, int64_t fb0, GemmScales& sc, v16f (&acc)[4][4]) {
+    GemmFrags f0, f1;
+    gemm_read<S>(f0, 0, lane, wm, wn);
+    gemm_read<S>(f1, 1, lane, wm, wn);
+    gemm_mfma<0>(f0, sc, acc);
+    gemm_read<S>(f0, 2, lane, wm, wn);
+    gemm_mfma<1>(f1, sc, acc);
+    gemm_read<S>(f1, 3, lane, wm, wn);
+    gemm_mfma<2>(f0, sc, acc);
+    gemm_mfma<3>(f1, sc, acc);
+    gemm_wait_barrier<0>();
+    gemm_issue<S>(p, L, min(t + 2, p.steps - 1), wave, fa0, fb0, sc);
+    // keep the scheduler from sinking the scale loads towards their use in
+    // the step after next (their latency would then show at the next wait)
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Store a wave's 128 x 128 quarter (rows r0.., columns c0.. of C) through
+// its own LDS region, 32 rows at a time.  Lane l holds row 32 i + l % 32 and
+// columns 32 j + 8 g + 4 (l / 32) + 0..3 in acc[i][j][4 g ..].  In LDS the
+// 16-byte chunks of a row are XOR-swizzled by the row.
+template <class T>
+__device__ __forceinline__ void gemm_store(const GemmArgs& p, const v16f (&acc)[4][4], uint8_t* buf, int64_t r0,
+                                           int64_t c0, int lane, bool full) {
+    constexpr int kVals = 16 / sizeof(T);        // values per 16-byte chunk
+    constexpr int kRowChunks = 128 / kVals;      // chunks per 128-column row
+    constexpr int kRowBytes = 128 * sizeof(T);
+    constexpr int kRowsPerPass = 64 / kRowChunks;
+    const int rr = lane & 31, hi = lane >> 5;
+    T* c = reinterpret_cast<T*>(p.c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = 32 * j + 8 * g + 4 * hi;           // first of the lane's 4 columns
+                const int chunk = col / kVals, part = col % kVals;
+                uint8_t* dst = buf + rr * kRowBytes + 16 * (chunk ^ (rr % kRowChunks)) + part * (int)sizeof(T);
+                if constexpr (sizeof(T) == 4) {
+                    *reinterpret_cast<v4i*>(dst) = v4i{__float_as_int(acc[i][j][4 * g]),
+                                                       __float_as_int(acc[i][j][4 * g + 1]),
+                                                       __float_as_int(acc[i][j][4 * g + 2]),
+                                                       __float_as_int(acc[i][j][4 * g + 3])};
+                } else {
+                    *reinterpret_cast<v2i*>(dst) =
+                        v2i{(int)pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                            (int)pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+                }
+            }
+#pragma unroll
+        for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
+            const int row = kRowsPerPass * pass + lane / kRowChunks, q = lane % kRowChunks;
+            const v4i v = *reinterpret_cast<const v4i*>(buf + row * kRowBytes + 16 * (q ^ (row % kRowChunks)));
+            const int64_t grow = r0 + 32 * i + row, gcol = c0 + q * kVals;
+            T* out = c + grow * p.ldc + gcol;
+            if (full || (grow < p.M && gcol + kVals <= p.N)) {
+                *reinterpret_cast<v4i*>(out) = v;
+            } else if (grow < p.M) {
+                const T* e = reinterpret_cast<const T*>(&v);
+                for (int k = 0; k < kVals; ++k)
+                    if (gcol + k < p.N) out[k] = e[k];
+            }
+        }
+    }
+}
+
+// PARITY = steps % 2: an odd step count runs its first step ahead of the
+// pairs, so the loop body is a whole number of stage pairs.
+template <int PARITY>
 __global__ __launch_bounds__(256, 1) void k_mxfp4_gemm(GemmArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     int tm, tn;
     gemm_tile(p, tm, tn);
-    const int64_t m0 = (int64_t)tm * kGemmTileM, n0 = (int64_t)tn * kGemmTileN;
-    const int nk = (int)(p.K / kGemmK);
+    const int64_t m0 = (int64_t)tm * kGemmTile, n0 = (int64_t)tn * kGemmTile;
+    const int64_t fa0 = (m0 + 128 * wm) / 32, fb0 = (n0 + 128 * wn) / 32;
+    const int nt = p.steps;
 
-    v4f acc[8][8];
+    v16f acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    // slices 0 .. 2 in flight before the first step (a short K reloads its last slice)
-    gemm_issue_slice<0>(p, m0, n0, 0, wave, lane);
-    gemm_issue_slice<1>(p, m0, n0, min(1, nk - 1), wave, lane);
-    gemm_issue_slice<2>(p, m0, n0, min(2, nk - 1), wave, lane);
+    // steps 0 and 1 in flight (a single step reloads itself), wait for step 0
+    const GemmLane L = gemm_lane(p, m0, n0, wave, lane, wm, wn);
+    GemmScales s0, s1;
+    gemm_issue<0>(p, L, 0, wave, fa0, fb0, s0);
+    gemm_issue<1>(p, L, min(1, nt - 1), wave, fa0, fb0, s1);
+    gemm_wait_barrier<kGemmLoadsPerStep>();
+    if constexpr (PARITY == 1) {
+        gemm_step<0>(p, L, 0, wave, lane, wm, wn, fa0, fb0, s0, acc);
 #pragma unroll 1
-    for (int ks = 0; ks < nk; ks += kGemmStages) {
-        gemm_step<0>(p, m0, n0, ks, nk, wave, lane, wm, wn, acc);
-        gemm_step<1>(p, m0, n0, ks + 1, nk, wave, lane, wm, wn, acc);
-        gemm_step<2>(p, m0, n0, ks + 2, nk, wave, lane, wm, wn, acc);
-        gemm_step<3>(p, m0, n0, ks + 3, nk, wave, lane, wm, wn, acc);
-    }
-    gemm_wait_barrier<0>();                      // no direct load outlives the kernel
-
-    // result lane l holds column l % 16 of rows 4 (l / 16) .. + 3 of each fragment
-    const int fr = lane & 15, kb = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t col = n0 + wn * 128 + 16 * j + fr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * 128 + 16 * i + 4 * kb + r;
-                if (row < p.M && col < p.N) {
-                    if (p.c_dt == DT_F32) reinterpret_cast<float*>(p.c)[row * p.ldc + col] = acc[i][j][r];
-                    else reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] =
-                        (uint16_t)(pack_bf16x2(acc[i][j][r], 0.0f) & 0xFFFFu);
-                }
-            }
+        for (int t = 1; t < nt; t += 2) {
+            gemm_step<1>(p, L, t, wave, lane, wm, wn, fa0, fb0, s1, acc);
+            gemm_step<0>(p, L, t + 1, wave, lane, wm, wn, fa0, fb0, s0, acc);
         }
+    } else {
+#pragma unroll 1
+        for (int t = 0; t < nt; t += 2) {
+            gemm_step<0>(p, L, t, wave, lane, wm, wn, fa0, fb0, s0, acc);
+            gemm_step<1>(p, L, t + 1, wave, lane, wm, wn, fa0, fb0, s1, acc);
+        }
+    }
+    // The last step waited for every load it issued but one step's worth,
+    // and re-issued loads past the end: drain them before reusing stage 0.
+    gemm_wait_barrier<0>();
+    uint8_t* buf = reinterpret_cast<uint8_t*>(&g_stage0) + wave * (32 * 128 * 4);
+    const int64_t r0 = m0 + 128 * wm, c0 = n0 + 128 * wn;
+    const bool full = m0 + kGemmTile <= p.M && n0 + kGemmTile <= p.N;
+    if (p.c_dt == DT_F32) gemm_store<float>(p, acc, buf, r0, c0, lane, full);
+    else gemm_store<uint16_t>(p, acc, buf, r0, c0, lane, full);
+}
+
+size_t mxfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+    const int64_t steps = K / kGemmStepK;
+    const auto part = [&](int64_t rows) { return (size_t)((((rows + 31) / 32) * steps * 256 + 255) / 256 * 256); };
+    return part(M) + part(N);
 }
 
 hipError_t launch_mxfp4_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
-                             int64_t N, int64_t K, void* c, int c_dt, int64_t ldc, hipStream_t s) {
+                             int64_t N, int64_t K, void* c, int c_dt, int64_t ldc, void* workspace, hipStream_t s) {
     GemmArgs p{};
     p.a = a;
-    p.as = as;
     p.b = b;
-    p.bs = bs;
     p.M = M;
     p.N = N;
     p.K = K;
     p.c = c;
     p.c_dt = c_dt;
     p.ldc = ldc;
-    p.tiles_m = (int)((M + kGemmTileM - 1) / kGemmTileM);
-    p.tiles_n = (int)((N + kGemmTileN - 1) / kGemmTileN);
-    hipLaunchKernelGGL(k_mxfp4_gemm, dim3((unsigned)p.tiles_m * p.tiles_n), dim3(256), 0, s, p);
+    p.tiles_m = (int)((M + kGemmTile - 1) / kGemmTile);
+    p.tiles_n = (int)((N + kGemmTile - 1) / kGemmTile);
+    p.steps = (int)(K / kGemmStepK);
+    p.frags_a = (int)((M + 31) / 32);
+    p.frags_b = (int)((N + 31) / 32);
+    const size_t wa = ((size_t)p.frags_a * p.steps * 256 + 255) / 256 * 256;
+    uint32_t* sa = reinterpret_cast<uint32_t*>(workspace);
+    uint32_t* sb = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(workspace) + wa);
+    const int64_t ta = (int64_t)p.frags_a * p.steps * 64, tb = (int64_t)p.frags_b * p.steps * 64;
+    hipLaunchKernelGGL(k_gemm_shuffle_scales, dim3((unsigned)((ta + 255) / 256)), dim3(256), 0, s, as, M, K / 32,
+                       p.steps, ta, sa);
+    hipLaunchKernelGGL(k_gemm_shuffle_scales, dim3((unsigned)((tb + 255) / 256)), dim3(256), 0, s, bs, N, K / 32,
+                       p.steps, tb, sb);
+    p.sa = sa;
+    p.sb = sb;
+    const dim3 grid((unsigned)p.tiles_m * p.tiles_n), block(256);
+    if (p.steps % 2) hipLaunchKernelGGL(k_mxfp4_gemm<1>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(k_mxfp4_gemm<0>, grid, block, 0, s, p);
     return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "libfp4q.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "fp4q.h")
 
 # FP4Q_ABI_VERSION and the enums (include/fp4q.h)
-ABI_VERSION = 2
+ABI_VERSION = 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE = range(6)
 F32, BF16, F16 = 0, 1, 2
 E8M0, E4M3, UE5M3 = 0, 1, 2
@@ -97,7 +97,9 @@ def lib() -> ctypes.CDLL:
         L.fp4q_code_histogram.restype = ctypes.c_int
         L.fp4q_code_histogram.argtypes = [p, i64, i64, p, p]
         L.fp4q_mxfp4_gemm.restype = ctypes.c_int
-        L.fp4q_mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, ctypes.c_int, i64, p]
+        L.fp4q_mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, ctypes.c_int, i64, p, p]
+        L.fp4q_mxfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
+        L.fp4q_mxfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         _lib = L
     return _lib
 
@@ -217,11 +219,15 @@ def fp4q_code_histogram(codes, counts, stream=None):
     _check(st, "fp4q_code_histogram")
 
 
-def fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, stream=None):
+def mxfp4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().fp4q_mxfp4_gemm_workspace_bytes(M, N, K)
+
+
+def fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, workspace, stream=None):
     M, N = a_codes.shape[0], b_codes.shape[0]
     K = 2 * a_codes.shape[1]
     st = lib().fp4q_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K, _ptr(c),
-                               dtype_code(c), c.stride(0), _stream(stream))
+                               dtype_code(c), c.stride(0), _ptr(workspace), _stream(stream))
     _check(st, "fp4q_mxfp4_gemm")
 
 
@@ -294,8 +300,16 @@ def code_histogram(codes, stream=None):
     return counts
 
 
-def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.float32, stream=None):
+def gemm_workspace(M, N, K, device):
+    """Device workspace for fp4q_mxfp4_gemm (256-byte aligned by torch's allocator)."""
+    return torch.empty(max(mxfp4_gemm_workspace_bytes(M, N, K), 256), dtype=torch.uint8, device=device)
+
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.float32, workspace=None, stream=None):
     """C [M, N] = dq(A) dq(B)^T for MXFP4 operands (codes [rows, K/2], E8M0 scales [rows, K/32])."""
-    c = torch.empty((a_codes.shape[0], b_codes.shape[0]), dtype=out_dtype, device=a_codes.device)
-    fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, stream)
+    M, N, K = a_codes.shape[0], b_codes.shape[0], 2 * a_codes.shape[1]
+    c = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    if workspace is None:
+        workspace = gemm_workspace(M, N, K, a_codes.device)
+    fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, workspace, stream)
     return c

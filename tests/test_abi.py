@@ -9,7 +9,6 @@ GPU device node exists.
 """
 import ctypes
 import os
-
 import re
 
 import pytest

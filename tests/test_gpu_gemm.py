@@ -2,11 +2,13 @@
 oracle's fp64 product C = dq(A) dq(B)^T.
 
 Tolerance, from the arithmetic: every product of two decoded MXFP4 values
-is exact in fp32 (at most 2 x 2 significant bits times a power of two), the
-matrix core adds the 128 products of one instruction and the running sum,
-and the running fp32 sum is rounded once per 128-long K step.  So
-|C_gpu - C| <= (K/128 + 1) * 2^-24 * sum_k |a_k b_k|; the test allows twice
-that.  bf16 output adds the final rounding (2^-8 relative)."""
+is exact in fp32 (at most 2 x 2 significant bits times a power of two);
+one matrix-core instruction adds the 64 products of a 64-wide K substep to
+the running fp32 sum.  Allowing for an internal pairwise sum rounded at
+every level (depth 7 with the running sum) plus one rounding of the running
+sum per substep: |C_gpu - C| <= (K/64 + 8) * 2^-24 * sum_k |a_k b_k|; the
+test allows twice that.  bf16 output adds the final rounding (2^-8
+relative)."""
 import numpy as np
 import pytest
 import torch
@@ -44,15 +46,16 @@ def run_gpu(a, sa, b, sb, out=torch.float32):
 
 
 def check(got, want, bound_abs, K, bf16=False):
-    tol = 2 * (K / 128 + 1) * 2.0 ** -24 * bound_abs
+    tol = 2 * (K / 64 + 8) * 2.0 ** -24 * bound_abs
     if bf16:
         tol = tol + 2.0 ** -8 * np.abs(want)
     bad = np.abs(got - want) > tol
     assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:3].tolist())
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (256, 256, 1024), (512, 768, 512), (96, 200, 256),
-                                   (16, 16, 128), (300, 1000, 384)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (256, 256, 1024), (512, 768, 512), (96, 200, 256),
+                                   (16, 16, 256), (300, 1000, 768), (256, 256, 1280), (128, 512, 1792),
+                                   (520, 264, 2048)])
 def test_random_codes(O_lib, M, N, K):
     a, sa, b, sb = operands(M + N + K, M, N, K)
     note(f"gemm random {M}x{N}x{K}")
@@ -92,11 +95,58 @@ def test_wide_scale_range(O_lib):
     check(run_gpu(a, sa, b, sb), O.mxfp4_gemm(a, sa, b, sb), abs_product(a, sa, b, sb), 512)
 
 
+def test_ragged_n_padded_ldc(O_lib):
+    """N = 77 (not a whole 16-byte chunk of either output type) through a
+    padded C [M, 80]: the edge chunks are stored element by element and the
+    padding columns are left alone."""
+    M, N, K = 70, 77, 512
+    a, sa, b, sb = operands(21, M, N, K)
+    t = [torch.from_numpy(v).to(DEV) for v in (a, sa, b, sb)]
+    want = O.mxfp4_gemm(a, sa, b, sb)
+    bound = abs_product(a, sa, b, sb)
+    for dt in (torch.float32, torch.bfloat16):
+        note(f"gemm ragged N=77 ldc=80 {dt}")
+        full = torch.full((M, 80), 7.0, dtype=dt, device=DEV)
+        F.fp4q_mxfp4_gemm(*t, full[:, :N], F.gemm_workspace(M, N, K, DEV))
+        torch.cuda.synchronize()
+        got = full.float().cpu().numpy().astype(np.float64)
+        check(got[:, :N], want, bound, K, bf16=dt == torch.bfloat16)
+        assert np.all(got[:, N:] == 7.0)
+
+
+def test_full_size_sampled(O_lib):
+    """8192 x 8192 x 8192 with bf16 output, the shape the throughput is
+    measured on: sampled rows and columns against the oracle."""
+    M = N = K = 8192
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    a = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=DEV, generator=gen)
+    b = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=DEV, generator=gen)
+    sa = torch.randint(123, 132, (M, K // 32), dtype=torch.uint8, device=DEV, generator=gen)
+    sb = torch.randint(123, 132, (N, K // 32), dtype=torch.uint8, device=DEV, generator=gen)
+    note("gemm 8192^3 bf16")
+    c = F.mxfp4_gemm(a, sa, b, sb, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 2047, 4100, 8191])
+    cols = np.array([0, 255, 256, 5000, 8191])
+    an, san, bn, sbn = (v.cpu().numpy() for v in (a, sa, b, sb))
+    got = c.float().cpu().numpy().astype(np.float64)
+    want_r = O.mxfp4_gemm(an[rows], san[rows], bn, sbn)
+    check(got[rows], want_r, abs_product(an[rows], san[rows], bn, sbn), K, bf16=True)
+    want_c = O.mxfp4_gemm(an, san, bn[cols], sbn[cols])
+    check(got[:, cols], want_c, abs_product(an, san, bn[cols], sbn[cols]), K, bf16=True)
+
+
 def test_empty_and_validation(O_lib):
     L = F.lib()
     z = torch.zeros(64, dtype=torch.uint8, device=DEV)
     c = torch.zeros((4, 4), dtype=torch.float32, device=DEV)
+    ws = F.gemm_workspace(4, 4, 256, DEV)
     p = lambda t: t.data_ptr()
-    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 0, 4, 128, p(c), F.F32, 4, None) == F.OK
-    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 100, p(c), F.F32, 4, None) == F.ERR_SHAPE
-    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 128, p(c), F.F16, 4, None) == F.ERR_INVALID_ARG
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 0, 4, 256, p(c), F.F32, 4, p(ws), None) == F.OK
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 128, p(c), F.F32, 4, p(ws), None) == F.ERR_SHAPE
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 0, p(c), F.F32, 4, p(ws), None) == F.ERR_SHAPE
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 256, p(c), F.F16, 4, p(ws), None) == F.ERR_INVALID_ARG
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 256, p(c), F.F32, 4, None, None) == F.ERR_INVALID_ARG
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 256, p(c), F.F32, 4, p(ws) + 16, None) == \
+        F.ERR_ALIGNMENT
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 256, p(c), F.F32, 3, p(ws), None) == F.ERR_SHAPE
