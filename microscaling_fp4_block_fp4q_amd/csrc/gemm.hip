@@ -21,8 +21,10 @@
 // rows x 128 bytes of A and of B) go straight from global memory into one of
 // two LDS stages with the direct loads, each load reading 8 whole 128-byte
 // rows; the next step's load runs while the current step computes.  Within a
-// row the eight 16-byte chunks are stored XOR-swizzled by the row, so both
-// the direct-load writes and the fragment reads are free of bank conflicts.
+// row the eight 16-byte chunks are stored XOR-swizzled by the row pair, so
+// both the direct-load writes and the fragment reads are free of bank
+// conflicts (a 16-byte read serves 16 lanes at a time from the 64 banks,
+// i.e. two 128-byte rows).
 //
 // Scales: a small pass first rewrites each operand's [rows, K/32] scale bytes
 // into the per-lane dwords the MFMA takes (for fragment f, step t, lane l:
@@ -123,7 +125,7 @@ __device__ __forceinline__ void gemm_wait_barrier() {
 // One step's codes.  Two stages, as two separate objects: the compiler tracks
 // the direct loads per LDS object, so reading one stage does not make it wait
 // for the loads still filling the other.  Row r's chunk c (16 bytes, K block
-// c of the step) sits at r * 128 + 16 (c ^ (r % 8)).
+// c of the step) sits at r * 128 + 16 (c ^ (r / 2 % 8)).
 struct GemmStage {
     uint8_t a[kGemmOperandBytes];
     uint8_t b[kGemmOperandBytes];
@@ -146,16 +148,18 @@ struct GemmLane {
 
 // Direct load q of wave w covers tile rows 8 (8 w + q) .. + 7, 1 KB of LDS:
 // lane l writes 16 bytes at + 16 l, i.e. row 8 (8 w + q) + l / 8, slot l % 8,
-// which holds chunk (l % 8) ^ (row % 8) - the 8 lanes of a row read its whole
-// 128 bytes.  Rows past the matrix read its last row (results not stored).
+// which holds chunk (l % 8) ^ (row / 2 % 8) - the 8 lanes of a row read its
+// whole 128 bytes.  Rows past the matrix read its last row (results not
+// stored).
 __device__ __forceinline__ GemmLane gemm_lane(const GemmArgs& p, int64_t m0, int64_t n0, int wave, int lane,
                                               int wm, int wn) {
     const int64_t kbytes = p.K / 2;
-    const int sub = lane >> 3, chunk = (lane & 7) ^ (sub & 7);
+    const int sub = lane >> 3;
     GemmLane L;
 #pragma unroll
     for (int q = 0; q < kGemmDmaPerOperand; ++q) {
         const int r = 8 * (kGemmDmaPerOperand * wave + q) + sub;
+        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
         L.oa[q] = (uint32_t)(min<int64_t>(m0 + r, p.M - 1) * kbytes + 16 * chunk);
         L.ob[q] = (uint32_t)(min<int64_t>(n0 + r, p.N - 1) * kbytes + 16 * chunk);
     }
@@ -170,10 +174,9 @@ struct GemmScales {
     int a[4], b[4];
 };
 
-// Issue step t's loads: the codes into stage S, the scale dwords into sc.
+// Issue step t's direct loads of the codes into stage S.
 template <int S>
-__device__ __forceinline__ void gemm_issue(const GemmArgs& p, const GemmLane& L, int t, int wave, int64_t fa0,
-                                           int64_t fb0, GemmScales& sc) {
+__device__ __forceinline__ void gemm_issue_codes(const GemmArgs& p, const GemmLane& L, int t, int wave) {
     GemmStage& st = gemm_stage<S>();
     const uint8_t* a = p.a + (int64_t)t * kGemmRowBytes;
     const uint8_t* b = p.b + (int64_t)t * kGemmRowBytes;
@@ -183,6 +186,11 @@ __device__ __forceinline__ void gemm_issue(const GemmArgs& p, const GemmLane& L,
         __builtin_amdgcn_global_load_lds((const void*)(a + L.oa[q]), (lds_void_ptr)(st.a + j * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(b + L.ob[q]), (lds_void_ptr)(st.b + j * 1024), 16, 0, 0);
     }
+}
+
+// Load step t's scale dwords into sc.
+__device__ __forceinline__ void gemm_issue_scales(const GemmArgs& p, const GemmLane& L, int t, int64_t fa0,
+                                                  int64_t fb0, GemmScales& sc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t fa = min<int64_t>(fa0 + i, p.frags_a - 1) - fa0;
@@ -210,7 +218,7 @@ template <int S>
 __device__ __forceinline__ void gemm_read(GemmFrags& fr, int h, int lane, int wm, int wn) {
     const GemmStage& st = gemm_stage<S>();
     const int r = lane & 31;
-    const int slot = (2 * h + (lane >> 5)) ^ (r & 7);
+    const int slot = (2 * h + (lane >> 5)) ^ ((r >> 1) & 7);
     const int off = r * kGemmRowBytes + 16 * slot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -229,28 +237,59 @@ __device__ __forceinline__ void gemm_mfma(const GemmFrags& fr, const GemmScales&
                                                                         sc.b[j], H, sc.a[i]);
 }
 
-// Step t on stage S with scales sc: the four K substeps, each substep's
-// fragments read while the previous substep's MFMAs run.  Then wait for step
-// t + 1's loads, pass the barrier (every wave is done with stage S) and refill
-// stage S and sc with step t + 2 (re-reading the last step past the end, so
-// the direct loads stay outside any branch and the compiler adds no wait of
-// its own before the fragment reads).
+// Scheduling: one wave per SIMD cannot run ahead of its matrix pipe (an MFMA
+// issues only once the previous one is under way), so loads placed after a
+// run of MFMAs would show their latency in full.  The group barriers below
+// put one fragment read (DS) or direct load (VMEM) after each MFMA.
+template <int NREAD>
+__device__ __forceinline__ void gemm_sched_reads() {
+#pragma unroll
+    for (int k = 0; k < NREAD; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16 - NREAD, 0);
+}
+
+// Step t on stage S with scales sc; f0 holds substep 0's fragments (read
+// during the previous step).  Substeps 0..2 each read the next substep's
+// fragments while their MFMAs run.  Then wait for step t + 1's loads and
+// this wave's reads, pass the barrier (every wave is done with stage S and
+// step t + 1 is in LDS), and during substep 3 refill stage S with step t + 2
+// and read step t + 1's substep-0 fragments into f0; last, step t + 2's
+// scales into sc.  The refill runs on every step, also past the last one (it
+// then reloads the last step), so the direct loads stay outside any branch
+// and the compiler adds no wait of its own before the fragment reads.
 template <int S>
 __device__ __forceinline__ void gemm_step(const GemmArgs& p, const GemmLane& L, int t, int wave, int lane, int wm,
-                                          int wn, int64_t fa0, int64_t fb0, GemmScales& sc, v16f (&acc)[4][4]) {
-    GemmFrags f0, f1;
-    gemm_read<S>(f0, 0, lane, wm, wn);
+                                          int wn, int64_t fa0, int64_t fb0, GemmScales& sc, GemmFrags& f0,
+                                          v16f (&acc)[4][4]) {
+    GemmFrags f1;
     gemm_read<S>(f1, 1, lane, wm, wn);
     gemm_mfma<0>(f0, sc, acc);
+    gemm_sched_reads<8>();
+    __builtin_amdgcn_sched_barrier(0);
     gemm_read<S>(f0, 2, lane, wm, wn);
     gemm_mfma<1>(f1, sc, acc);
+    gemm_sched_reads<8>();
+    __builtin_amdgcn_sched_barrier(0);
     gemm_read<S>(f1, 3, lane, wm, wn);
     gemm_mfma<2>(f0, sc, acc);
-    gemm_mfma<3>(f1, sc, acc);
+    gemm_sched_reads<8>();
+    __builtin_amdgcn_sched_barrier(0);
     gemm_wait_barrier<0>();
-    gemm_issue<S>(p, L, min(t + 2, p.steps - 1), wave, fa0, fb0, sc);
-    // keep the scheduler from sinking the scale loads towards their use in
-    // the step after next (their latency would then show at the next wait)
+    gemm_issue_codes<S>(p, L, min(t + 2, p.steps - 1), wave);
+    gemm_read<S ^ 1>(f0, 0, lane, wm, wn);
+    gemm_mfma<3>(f1, sc, acc);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);   // two direct loads
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_issue_scales(p, L, min(t + 2, p.steps - 1), fa0, fb0, sc);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -325,21 +364,25 @@ __global__ __launch_bounds__(256, 1) void k_mxfp4_gemm(GemmArgs p) {
     // steps 0 and 1 in flight (a single step reloads itself), wait for step 0
     const GemmLane L = gemm_lane(p, m0, n0, wave, lane, wm, wn);
     GemmScales s0, s1;
-    gemm_issue<0>(p, L, 0, wave, fa0, fb0, s0);
-    gemm_issue<1>(p, L, min(1, nt - 1), wave, fa0, fb0, s1);
+    gemm_issue_codes<0>(p, L, 0, wave);
+    gemm_issue_scales(p, L, 0, fa0, fb0, s0);
+    gemm_issue_codes<1>(p, L, min(1, nt - 1), wave);
+    gemm_issue_scales(p, L, min(1, nt - 1), fa0, fb0, s1);
     gemm_wait_barrier<kGemmLoadsPerStep>();
+    GemmFrags f0;
+    gemm_read<0>(f0, 0, lane, wm, wn);
     if constexpr (PARITY == 1) {
-        gemm_step<0>(p, L, 0, wave, lane, wm, wn, fa0, fb0, s0, acc);
+        gemm_step<0>(p, L, 0, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
 #pragma unroll 1
         for (int t = 1; t < nt; t += 2) {
-            gemm_step<1>(p, L, t, wave, lane, wm, wn, fa0, fb0, s1, acc);
-            gemm_step<0>(p, L, t + 1, wave, lane, wm, wn, fa0, fb0, s0, acc);
+            gemm_step<1>(p, L, t, wave, lane, wm, wn, fa0, fb0, s1, f0, acc);
+            gemm_step<0>(p, L, t + 1, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
         }
     } else {
 #pragma unroll 1
         for (int t = 0; t < nt; t += 2) {
-            gemm_step<0>(p, L, t, wave, lane, wm, wn, fa0, fb0, s0, acc);
-            gemm_step<1>(p, L, t + 1, wave, lane, wm, wn, fa0, fb0, s1, acc);
+            gemm_step<0>(p, L, t, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
+            gemm_step<1>(p, L, t + 1, wave, lane, wm, wn, fa0, fb0, s1, f0, acc);
         }
     }
     // The last step waited for every load it issued but one step's worth,
