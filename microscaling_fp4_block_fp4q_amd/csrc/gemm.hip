@@ -326,16 +326,23 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& p, const v16f (&acc)[
                             (int)pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
                 }
             }
+        // all reads of the block first, then the stores: one wait for LDS
+        constexpr int kPasses = 32 / kRowsPerPass;
+        v4i v[kPasses];
 #pragma unroll
-        for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
+        for (int pass = 0; pass < kPasses; ++pass) {
             const int row = kRowsPerPass * pass + lane / kRowChunks, q = lane % kRowChunks;
-            const v4i v = *reinterpret_cast<const v4i*>(buf + row * kRowBytes + 16 * (q ^ (row % kRowChunks)));
+            v[pass] = *reinterpret_cast<const v4i*>(buf + row * kRowBytes + 16 * (q ^ (row % kRowChunks)));
+        }
+#pragma unroll
+        for (int pass = 0; pass < kPasses; ++pass) {
+            const int row = kRowsPerPass * pass + lane / kRowChunks, q = lane % kRowChunks;
             const int64_t grow = r0 + 32 * i + row, gcol = c0 + q * kVals;
             T* out = c + grow * p.ldc + gcol;
             if (full || (grow < p.M && gcol + kVals <= p.N)) {
-                *reinterpret_cast<v4i*>(out) = v;
+                *reinterpret_cast<v4i*>(out) = v[pass];
             } else if (grow < p.M) {
-                const T* e = reinterpret_cast<const T*>(&v);
+                const T* e = reinterpret_cast<const T*>(&v[pass]);
                 for (int k = 0; k < kVals; ++k)
                     if (gcol + k < p.N) out[k] = e[k];
             }
