@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--only", default=None,
                     help="profiling mode: run only the calls whose name contains one of these "
                          "'|'-separated texts, --steps times, and print no result line")
+    ap.add_argument("--profile-gemm", action="store_true",
+                    help="profiling mode: run only the 8192^3 MXFP4 GEMM, --steps times, and print no result line")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="profiling mode: also run a device-to-device copy of this many MiB "
                          "(calibrates the HBM byte counters)")
@@ -85,12 +87,17 @@ class Call:
             raise RuntimeError(f"{self.name}: status {st}")
 
 
-def source_digest() -> str:
-    """sha256 over the HIP sources and headers (ties counter profiles to a kernel version)."""
+GEMM_SOURCES = ("gemm.hip",)
+
+
+def source_digest(gemm: bool = False) -> str:
+    """sha256 over the HIP sources and headers (ties counter profiles to a
+    kernel version): the GEMM's own source for gemm=True, else every other
+    one (the quantize path)."""
     import hashlib
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp")):
+        if f.endswith((".hip", ".hpp")) and (f in GEMM_SOURCES) == gemm:
             with open(os.path.join(CSRC, f), "rb") as fh:
                 h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -101,7 +108,8 @@ def summarize(dirs, label, command):
     into profiles/<label>.json (numbers) and profiles/<label>.md (table)."""
     import csv
     import glob
-    out = {"label": label, "command": command, "source_digest": source_digest(), "kernels": {}, "counters": {}}
+    gemm = "gemm" in label
+    out = {"label": label, "command": command, "source_digest": source_digest(gemm), "kernels": {}, "counters": {}}
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
@@ -168,6 +176,32 @@ def counter_traffic(kernel_name: str):
     f_scale = copy_kib / copy["FETCH_SIZE"]["mean"]
     w_scale = copy_kib / copy["WRITE_SIZE"]["mean"]
     return 1024.0 * (kern["FETCH_SIZE"]["mean"] * f_scale + kern["WRITE_SIZE"]["mean"] * w_scale)
+
+
+def gemm_profile():
+    """The committed kernel-stat and counter profiles of the 8192^3 GEMM, if
+    they were taken on the current GEMM source."""
+    out = {}
+    for label in ("kernel_stats_mxfp4_gemm_8192", "counters_mxfp4_gemm_8192"):
+        path = os.path.join(PROFILES, label + ".json")
+        if not os.path.exists(path):
+            continue
+        prof = json.load(open(path))
+        if prof.get("source_digest") != source_digest(gemm=True):
+            continue
+        for k, v in prof.get("kernels", {}).items():
+            if "k_mxfp4_gemm" in k:
+                out["avg_kernel_us"] = v["avg_us"]
+            elif "shuffle_scales" in k:
+                out["avg_shuffle_us"] = v["avg_us"]
+        for k, cs in prof.get("counters", {}).items():
+            if "k_mxfp4_gemm" in k:
+                out.update({c: v["mean"] for c, v in cs.items()})
+            elif "copyBuffer" in k:
+                out.update({"copy_" + c: v["mean"] for c, v in cs.items()})
+        if "copy_mib" in prof:
+            out["copy_mib"] = prof["copy_mib"]
+    return out
 
 
 def quant_bytes(rows, cols, B, in_es=4, dq_es=4, mse=True, dq=True):
@@ -342,6 +376,67 @@ def time_histogram(F, torch, x, reps=10):
                     "scale) codes of the 4096x4096 N(0,1) input, 8 MiB of code bytes"}
 
 
+MFMA_FP4_PEAK_TFLOPS = 10100.0              # MI355X dense FP4 matrix peak, published
+
+
+def time_gemm(F, torch, dev, warm=30, reps=10, rounds=3):
+    """MXFP4 GEMM (outside the step): C = dq(A) dq(B)^T with A the MXFP4
+    quantization of N(0,1) activations [tokens, in] and B that of N(0, 0.02^2)
+    weights [out, in], bf16 C.  Each call also rearranges both scale tensors
+    for the matrix cores.  Mean over rounds x reps calls after a warm-up, HIP
+    events on the library's stream; 2 M N K flops per call."""
+    out = {}
+    gen = torch.Generator(device=dev).manual_seed(11)
+    for M, N, K in ((8192, 8192, 8192), (8192, 14336, 4096), (8192, 4096, 14336)):
+        qa = F.quantize(torch.randn((M, K), generator=gen, device=dev), F.mxfp4(), want_mse=False)
+        qb = F.quantize(torch.randn((N, K), generator=gen, device=dev) * 0.02, F.mxfp4(), want_mse=False)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = F.gemm_workspace(M, N, K, dev)
+        args = (qa["codes"], qa["scales"], qb["codes"], qb["scales"], c, ws)
+        for _ in range(warm):
+            F.fp4q_mxfp4_gemm(*args)
+        ev = []
+        for _ in range(rounds * reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            F.fp4q_mxfp4_gemm(*args)
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out[f"{M}x{N}x{K}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                               "mfma_frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4)}
+        if M == N == K == 8192:
+            alg = M * K // 2 + N * K // 2 + (M + N) * K // 32 + M * N * 2
+            prof = gemm_profile()
+            roof = {"bound": "mfma", "kernel": "k_mxfp4_gemm<0> (+ 2 k_gemm_shuffle_scales)",
+                    "achieved": round(tf, 1), "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4), "avg_launch_ms": round(ms, 4),
+                    "algorithmic_MB_per_launch": round(alg / 1e6, 2), "traffic": None}
+            if "avg_kernel_us" in prof:
+                roof["profile_kernel_only_us"] = prof["avg_kernel_us"]
+                roof["profile_shuffle_us"] = prof.get("avg_shuffle_us")
+            if "FETCH_SIZE" in prof and "WRITE_SIZE" in prof and "copy_FETCH_SIZE" in prof:
+                kib = prof.get("copy_mib", 256) * 1024.0
+                t = 1024.0 * (prof["FETCH_SIZE"] * kib / prof["copy_FETCH_SIZE"] +
+                              prof["WRITE_SIZE"] * kib / prof["copy_WRITE_SIZE"])
+                roof["traffic"] = round(t / 1e6, 2)
+                roof["traffic_unit"] = "MB per launch of the GEMM kernel (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in prof and "GRBM_GUI_ACTIVE" in prof:
+                # busy cycles summed over the 1024 SIMDs; GRBM_GUI_ACTIVE summed over the 8 XCDs
+                roof["mfma_busy_frac"] = round(prof["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 /
+                                               (prof["GRBM_GUI_ACTIVE"] / 8), 4)
+            out["roofline_8192"] = roof
+        del qa, qb, c, ws, args
+    out["peak"] = {"TFLOP/s": MFMA_FP4_PEAK_TFLOPS, "what": "MI355X dense FP4 matrix-core peak"}
+    out["what"] = ("not part of the step: MXFP4 GEMM (M x N x K) of MXFP4-quantized N(0,1) activations and "
+                   "N(0,0.02^2) weights on the block-scaled 32x32x64 matrix cores, bf16 output, including the "
+                   "per-call scale rearrangement; mean of 30 calls after 30 warm-up calls")
+    return out
+
+
 def cpu_baseline(O, S, host, rows_per_tensor):
     """The oracle (single thread) on the first rows of every tensor, over the
     same call list as one GPU step."""
@@ -393,6 +488,26 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_gemm:
+        gen = torch.Generator(device=dev).manual_seed(11)
+        M = N = K = 8192
+        qa = F.quantize(torch.randn((M, K), generator=gen, device=dev), F.mxfp4(), want_mse=False)
+        qb = F.quantize(torch.randn((N, K), generator=gen, device=dev) * 0.02, F.mxfp4(), want_mse=False)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = F.gemm_workspace(M, N, K, dev)
+        torch.cuda.synchronize()
+        if args.copy_mb:
+            src = torch.empty(args.copy_mb << 18, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            src.fill_(1.0)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            F.fp4q_mxfp4_gemm(qa["codes"], qa["scales"], qb["codes"], qb["scales"], c, ws)
+            if args.copy_mb:
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] profiling run done", file=sys.stderr, flush=True)
+        return
     print("[bench] generating and uploading the workload", file=sys.stderr, flush=True)
     calls, keep, host, X = build_step(F, S, torch, dev)
     step_bytes = sum(c.nbytes for c in calls)
@@ -521,6 +636,7 @@ def main():
     ue5m3 = time_quantize_configs(F, torch, X["normal"], [
         (f"B={B} {STRATS[st]}", F.config(F.UE5M3, B, st)) for B in (16, 4) for st in (0, 2, 3)])
     hist = time_histogram(F, torch, X["normal"])
+    gemm = time_gemm(F, torch, dev)
     stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
     sb = sum(c.nbytes for c, _ in stream_quant)
     sms = sum(ms for _, ms in stream_quant)
@@ -556,6 +672,7 @@ def main():
         "ue5m3_scales": dict(ue5m3, what="not part of the step: quantize of the 4096x4096 N(0,1) input with "
                                          "UE5M3 block scales (no per-tensor scale), every output"),
         "code_histogram": hist,
+        "mxfp4_gemm": gemm,
         "copy_reference": {"GB/s": round(copy_gbs, 1), "hbm_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
                            "what": "device copy (read + write bytes) of the four 64 MiB inputs in rotation, "
                                    "the same access pattern as the quantize calls; per_strategy frac_of_copy "
