@@ -141,7 +141,8 @@ __device__ __forceinline__ GemmStage& gemm_stage() {
 
 // Per-lane state fixed for the whole K loop.
 struct GemmLane {
-    uint32_t oa[kGemmDmaPerOperand], ob[kGemmDmaPerOperand];   // direct-load byte offsets
+    __amdgpu_buffer_rsrc_t ra, rb;               // buffer descriptors of the A and B codes
+    uint32_t oa[kGemmDmaPerOperand], ob[kGemmDmaPerOperand];   // direct-load byte offsets in them
     const uint32_t* sa;                          // scale dwords of this wave's first A fragment, step 0
     const uint32_t* sb;
 };
@@ -156,6 +157,10 @@ __device__ __forceinline__ GemmLane gemm_lane(const GemmArgs& p, int64_t m0, int
     const int64_t kbytes = p.K / 2;
     const int sub = lane >> 3;
     GemmLane L;
+    // raw buffers (stride 0) over the code arrays; sizes are below 2^32
+    // bytes, and every offset below stays inside them
+    L.ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.a, (short)0, (int)(uint32_t)(p.M * kbytes), 0x00020000);
+    L.rb = __builtin_amdgcn_make_buffer_rsrc((void*)p.b, (short)0, (int)(uint32_t)(p.N * kbytes), 0x00020000);
 #pragma unroll
     for (int q = 0; q < kGemmDmaPerOperand; ++q) {
         const int r = 8 * (kGemmDmaPerOperand * wave + q) + sub;
@@ -174,17 +179,18 @@ struct GemmScales {
     int a[4], b[4];
 };
 
-// Issue step t's direct loads of the codes into stage S.
+// Issue step t's direct loads of the codes into stage S: buffer loads with
+// the per-lane offset fixed for the loop and the step's K offset in a scalar
+// register, so a load needs no address arithmetic of its own.
 template <int S>
-__device__ __forceinline__ void gemm_issue_codes(const GemmArgs& p, const GemmLane& L, int t, int wave) {
+__device__ __forceinline__ void gemm_issue_codes(const GemmLane& L, int t, int wave) {
     GemmStage& st = gemm_stage<S>();
-    const uint8_t* a = p.a + (int64_t)t * kGemmRowBytes;
-    const uint8_t* b = p.b + (int64_t)t * kGemmRowBytes;
+    const uint32_t koff = (uint32_t)t * kGemmRowBytes;
 #pragma unroll
     for (int q = 0; q < kGemmDmaPerOperand; ++q) {
         const int j = kGemmDmaPerOperand * wave + q;
-        __builtin_amdgcn_global_load_lds((const void*)(a + L.oa[q]), (lds_void_ptr)(st.a + j * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(b + L.ob[q]), (lds_void_ptr)(st.b + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.ra, (lds_void_ptr)(st.a + j * 1024), 16, L.oa[q], koff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rb, (lds_void_ptr)(st.b + j * 1024), 16, L.ob[q], koff, 0, 0);
     }
 }
 
@@ -278,7 +284,7 @@ __device__ __forceinline__ void gemm_step(const GemmArgs& p, const GemmLane& L, 
     gemm_sched_reads<8>();
     __builtin_amdgcn_sched_barrier(0);
     gemm_wait_barrier<0>();
-    gemm_issue_codes<S>(p, L, min(t + 2, p.steps - 1), wave);
+    gemm_issue_codes<S>(L, min(t + 2, p.steps - 1), wave);
     gemm_read<S ^ 1>(f0, 0, lane, wm, wn);
     gemm_mfma<3>(f1, sc, acc);
 #pragma unroll
@@ -354,7 +360,8 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& p, const v16f (&acc)[
 // pairs, so the loop body is a whole number of stage pairs.
 template <int PARITY>
 __global__ __launch_bounds__(256, 1) void k_mxfp4_gemm(GemmArgs p) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS addresses in scalars
     const int wm = wave >> 1, wn = wave & 1;
     int tm, tn;
     gemm_tile(p, tm, tn);
@@ -371,9 +378,9 @@ __global__ __launch_bounds__(256, 1) void k_mxfp4_gemm(GemmArgs p) {
     // steps 0 and 1 in flight (a single step reloads itself), wait for step 0
     const GemmLane L = gemm_lane(p, m0, n0, wave, lane, wm, wn);
     GemmScales s0, s1;
-    gemm_issue_codes<0>(p, L, 0, wave);
+    gemm_issue_codes<0>(L, 0, wave);
     gemm_issue_scales(p, L, 0, fa0, fb0, s0);
-    gemm_issue_codes<1>(p, L, min(1, nt - 1), wave);
+    gemm_issue_codes<1>(L, min(1, nt - 1), wave);
     gemm_issue_scales(p, L, min(1, nt - 1), fa0, fb0, s1);
     gemm_wait_barrier<kGemmLoadsPerStep>();
     GemmFrags f0;
