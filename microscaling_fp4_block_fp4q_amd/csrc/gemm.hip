@@ -48,9 +48,6 @@ constexpr int kGemmStepK = 256;                  // K per step: 8 scale blocks
 constexpr int kGemmRowBytes = kGemmStepK / 2;    // code bytes of a row per step
 constexpr int kGemmOperandBytes = kGemmTile * kGemmRowBytes;   // 32 KB
 constexpr int kGemmDmaPerOperand = kGemmOperandBytes / 1024 / 4;  // direct loads per wave
-// Vector-memory operations a wave issues per step: the direct loads of A and
-// B and the 8 scale-dword loads (4 A fragments, 4 B fragments).
-constexpr int kGemmLoadsPerStep = 2 * kGemmDmaPerOperand + 8;
 
 struct GemmArgs {
     const uint8_t* a;
@@ -182,12 +179,12 @@ struct GemmScales {
 // Issue step t's direct loads of the codes into stage S: buffer loads with
 // the per-lane offset fixed for the loop and the step's K offset in a scalar
 // register, so a load needs no address arithmetic of its own.
-template <int S>
+template <int S, int Q0 = 0, int Q1 = kGemmDmaPerOperand>
 __device__ __forceinline__ void gemm_issue_codes(const GemmLane& L, int t, int wave) {
     GemmStage& st = gemm_stage<S>();
     const uint32_t koff = (uint32_t)t * kGemmRowBytes;
 #pragma unroll
-    for (int q = 0; q < kGemmDmaPerOperand; ++q) {
+    for (int q = Q0; q < Q1; ++q) {
         const int j = kGemmDmaPerOperand * wave + q;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(L.ra, (lds_void_ptr)(st.a + j * 1024), 16, L.oa[q], koff, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rb, (lds_void_ptr)(st.b + j * 1024), 16, L.ob[q], koff, 0, 0);
@@ -257,23 +254,37 @@ __device__ __forceinline__ void gemm_sched_reads() {
     __builtin_amdgcn_sched_group_barrier(0x008, 16 - NREAD, 0);
 }
 
+constexpr int kHalfDma = kGemmDmaPerOperand / 2;
+
 // Step t on stage S with scales sc; f0 holds substep 0's fragments (read
 // during the previous step).  Substeps 0..2 each read the next substep's
-// fragments while their MFMAs run.  Then wait for step t + 1's loads and
-// this wave's reads, pass the barrier (every wave is done with stage S and
-// step t + 1 is in LDS), and during substep 3 refill stage S with step t + 2
+// fragments while their MFMAs run; substep 0 also issues the second half of
+// step t + 1's direct loads (into the other stage, free since the previous
+// barrier).  Then wait for step t + 1's loads and this wave's reads, pass the
+// barrier (every wave is done with stage S and step t + 1 is in LDS), and
+// during substep 3 issue the first half of step t + 2's loads into stage S
 // and read step t + 1's substep-0 fragments into f0; last, step t + 2's
-// scales into sc.  The refill runs on every step, also past the last one (it
-// then reloads the last step), so the direct loads stay outside any branch
-// and the compiler adds no wait of its own before the fragment reads.
+// scales into sc.  Spreading the direct loads over two substeps keeps the
+// four waves, which leave the barrier together, from queueing 64 loads at
+// once.  The loads run on every step, also past the last one (they then
+// reload the last step), so they stay outside any branch and the compiler
+// adds no wait of its own before the fragment reads.
 template <int S>
 __device__ __forceinline__ void gemm_step(const GemmArgs& p, const GemmLane& L, int t, int wave, int lane, int wm,
                                           int wn, int64_t fa0, int64_t fb0, GemmScales& sc, GemmFrags& f0,
                                           v16f (&acc)[4][4]) {
     GemmFrags f1;
+    // substep 0: the second half of step t + 1's direct loads into the other stage
+    gemm_issue_codes<S ^ 1, kHalfDma, kGemmDmaPerOperand>(L, min(t + 1, p.steps - 1), wave);
     gemm_read<S>(f1, 1, lane, wm, wn);
     gemm_mfma<0>(f0, sc, acc);
-    gemm_sched_reads<8>();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // direct load
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
     gemm_read<S>(f0, 2, lane, wm, wn);
     gemm_mfma<1>(f1, sc, acc);
@@ -284,13 +295,13 @@ __device__ __forceinline__ void gemm_step(const GemmArgs& p, const GemmLane& L, 
     gemm_sched_reads<8>();
     __builtin_amdgcn_sched_barrier(0);
     gemm_wait_barrier<0>();
-    gemm_issue_codes<S>(L, min(t + 2, p.steps - 1), wave);
+    gemm_issue_codes<S, 0, kHalfDma>(L, min(t + 2, p.steps - 1), wave);
     gemm_read<S ^ 1>(f0, 0, lane, wm, wn);
     gemm_mfma<3>(f1, sc, acc);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);   // two direct loads
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // direct load
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
@@ -375,14 +386,17 @@ __global__ __launch_bounds__(256, 1) void k_mxfp4_gemm(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    // steps 0 and 1 in flight (a single step reloads itself), wait for step 0
+    // step 0 and the first half of step 1 in flight (a single step reloads
+    // itself), wait for step 0
     const GemmLane L = gemm_lane(p, m0, n0, wave, lane, wm, wn);
     GemmScales s0, s1;
     gemm_issue_codes<0>(L, 0, wave);
     gemm_issue_scales(p, L, 0, fa0, fb0, s0);
-    gemm_issue_codes<1>(L, min(1, nt - 1), wave);
+    __builtin_amdgcn_sched_barrier(0);           // keep step 0's loads ahead of the wait count
+    gemm_issue_codes<1, 0, kHalfDma>(L, min(1, nt - 1), wave);
     gemm_issue_scales(p, L, min(1, nt - 1), fa0, fb0, s1);
-    gemm_wait_barrier<kGemmLoadsPerStep>();
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_wait_barrier<kGemmDmaPerOperand + 8>();    // all but step 1's half and its 8 scale loads
     GemmFrags f0;
     gemm_read<0>(f0, 0, lane, wm, wn);
     if constexpr (PARITY == 1) {
