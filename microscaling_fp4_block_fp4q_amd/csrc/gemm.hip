@@ -87,15 +87,15 @@ __global__ void k_gemm_shuffle_scales(const uint8_t* __restrict__ s, int64_t row
 }
 
 // Tile order: workgroups go round-robin to the 8 XCDs (blockIdx % 8), each
-// with its own L2.  Give XCD x a contiguous run of tiles, and walk tiles in
-// groups of 8 tile rows, so the 32 compute units of one XCD share few A and
-// B panels.
+// with its own L2.  XCD x runs the workgroups x, x + 8, ...: ntiles / 8 of
+// them, one more for x < ntiles % 8; give it that many consecutive tiles,
+// starting after the runs of the XCDs before it (a bijection onto the
+// tiles).  Tiles are numbered in groups of 8 tile rows, so the 32 compute
+// units of one XCD share few A and B panels.
 __device__ __forceinline__ void gemm_tile(const GemmArgs& p, int& tm, int& tn) {
     const int ntiles = p.tiles_m * p.tiles_n;
-    const int per_xcd = (ntiles + 7) / 8;
-    const int bid = blockIdx.x;
-    int t = (bid % 8) * per_xcd + bid / 8;
-    if (t >= ntiles) t = bid;                    // the uneven tail keeps the plain order
+    const int bid = blockIdx.x, x = bid % 8, q = ntiles / 8, r = ntiles % 8;
+    const int t = x * q + min(x, r) + bid / 8;
     constexpr int G = 8;
     const int in_group = G * p.tiles_n;
     const int first_m = (t / in_group) * G;
