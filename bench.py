@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements outside the step (scale search, UE5M3, histogram, GEMM)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="rows per tensor in the oracle sample")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--calls-out", default=None, help="write every call's mean time (ms) and bytes to this file")
@@ -630,13 +632,16 @@ def main():
     del dsts
     for k, v in breakdown.items():
         v["frac_of_copy"] = round(v["GB/s"] / copy_gbs, 4)
-    search = time_quantize_configs(F, torch, X["normal"], [
-        ("absmax", F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_SEARCH)),
-        ("4-over-6", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_SEARCH))])
-    ue5m3 = time_quantize_configs(F, torch, X["normal"], [
-        (f"B={B} {STRATS[st]}", F.config(F.UE5M3, B, st)) for B in (16, 4) for st in (0, 2, 3)])
-    hist = time_histogram(F, torch, X["normal"])
-    gemm = time_gemm(F, torch, dev)
+    if args.no_extras:
+        search = ue5m3 = hist = gemm = {"what": "not measured (--no-extras)"}
+    else:
+        search = time_quantize_configs(F, torch, X["normal"], [
+            ("absmax", F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_SEARCH)),
+            ("4-over-6", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_SEARCH))])
+        ue5m3 = time_quantize_configs(F, torch, X["normal"], [
+            (f"B={B} {STRATS[st]}", F.config(F.UE5M3, B, st)) for B in (16, 4) for st in (0, 2, 3)])
+        hist = time_histogram(F, torch, X["normal"])
+        gemm = time_gemm(F, torch, dev)
     stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
     sb = sum(c.nbytes for c, _ in stream_quant)
     sms = sum(ms for _, ms in stream_quant)
@@ -664,13 +669,13 @@ def main():
                                     "hbm_frac": round(sb / (sms * 1e6) / HBM_PEAK_GBS, 4),
                                     "frac_of_copy": round(sb / (sms * 1e6) / copy_gbs, 4)},
         "per_strategy": breakdown,
-        "global_scale_search": dict(search, what="not part of the step: NVFP4 block 16 quantize of the 4096x4096 "
-                                                 "N(0,1) input with the per-tensor scale searched over 32 "
-                                                 "candidates (abs-max pre-pass, 32-candidate scoring, tree "
-                                                 "reduction, pick, quantize at the winner); GB/s of the "
-                                                 "quantize call's algorithmic bytes"),
-        "ue5m3_scales": dict(ue5m3, what="not part of the step: quantize of the 4096x4096 N(0,1) input with "
-                                         "UE5M3 block scales (no per-tensor scale), every output"),
+        "global_scale_search": dict({"what": "not part of the step: NVFP4 block 16 quantize of the 4096x4096 "
+                                             "N(0,1) input with the per-tensor scale searched over 32 "
+                                             "candidates (abs-max pre-pass, 32-candidate scoring, tree "
+                                             "reduction, pick, quantize at the winner); GB/s of the "
+                                             "quantize call's algorithmic bytes"}, **search),
+        "ue5m3_scales": dict({"what": "not part of the step: quantize of the 4096x4096 N(0,1) input with "
+                                      "UE5M3 block scales (no per-tensor scale), every output"}, **ue5m3),
         "code_histogram": hist,
         "mxfp4_gemm": gemm,
         "copy_reference": {"GB/s": round(copy_gbs, 1), "hbm_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
