@@ -306,9 +306,14 @@ def gemm_workspace(M, N, K, device):
 
 
 def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.float32, workspace=None, stream=None):
-    """C [M, N] = dq(A) dq(B)^T for MXFP4 operands (codes [rows, K/2], E8M0 scales [rows, K/32])."""
+    """C [M, N] = dq(A) dq(B)^T for MXFP4 operands (codes [rows, K/2], E8M0 scales [rows, K/32]).
+
+    C is returned as a view of N columns of an [M, ldc] buffer whose rows are
+    padded to whole 16-byte chunks (the entry point's row alignment)."""
     M, N, K = a_codes.shape[0], b_codes.shape[0], 2 * a_codes.shape[1]
-    c = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    per16 = 16 // torch.empty(0, dtype=out_dtype).element_size()
+    ldc = (N + per16 - 1) // per16 * per16
+    c = torch.empty((M, ldc), dtype=out_dtype, device=a_codes.device)[:, :N]
     if workspace is None:
         workspace = gemm_workspace(M, N, K, a_codes.device)
     fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, workspace, stream)

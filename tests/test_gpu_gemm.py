@@ -55,7 +55,8 @@ def check(got, want, bound_abs, K, bf16=False):
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (256, 256, 1024), (512, 768, 512), (96, 200, 256),
                                    (16, 16, 256), (300, 1000, 768), (256, 256, 1280), (128, 512, 1792),
-                                   (520, 264, 2048), (640, 1000, 256), (2700, 600, 256), (2304, 2304, 256)])
+                                   (520, 264, 2048), (640, 1000, 256), (2700, 600, 256), (2304, 2304, 256),
+                                   (1, 1, 256), (1, 300, 512), (257, 1, 768)])
 def test_random_codes(O_lib, M, N, K):
     a, sa, b, sb = operands(M + N + K, M, N, K)
     note(f"gemm random {M}x{N}x{K}")
