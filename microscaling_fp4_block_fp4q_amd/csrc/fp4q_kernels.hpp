@@ -258,14 +258,15 @@ __device__ __forceinline__ float encode_block_at(const float (&y)[U], float S, f
 // Candidate scales of the brute-force search, one table per workgroup.
 // Entry c holds, for the scale S_c of code c (E4M3: fl(dec(c) g), c = 1..126;
 // E8M0: 2^(c-127), c = 0..254):
-//   x = S_c,  y = R_c (fl(1/S_c) when the division-free quotient applies,
-//   exact 2^(127-c) for E8M0),  z = T0_c, the largest fp32 a with
-//   fl(a / S_c) <= 0.25 (a that encodes to zero),  w = fl(6 S_c), the value a
-//   saturated element dequantizes to.
+//   sr = (S_c, R_c), R_c = fl(1/S_c) when the division-free quotient applies
+//   (exact 2^(127-c) for E8M0);  t0 = T0_c, the largest fp32 a with
+//   fl(a / S_c) <= 0.25 (a that encodes to zero);  six = fl(6 S_c), the value
+//   a saturated element dequantizes to.
 struct BfTable {
     static constexpr int kPad = 8;   // entries past the last code, read by padded work items
     float2 sr[256 + kPad];           // (S_c, R_c)
     float t0[256];                   // T0_c
+    float six[256];                  // fl(6 S_c)
     bool fast;                       // every candidate in the division-free range
 };
 
@@ -293,10 +294,13 @@ __device__ __forceinline__ void fill_bf_table(BfTable& t, float g) {
         }
         t.sr[c] = make_float2(S, R);
         t.t0[c] = zero_bin_limit(S);
+        t.six[c] = 6.0f * S;
     }
-    // codes past the last one: harmless values for work items padded to a
-    // whole number of candidates (their results are discarded)
-    for (uint32_t c = N + threadIdx.x; c < 256u + BfTable::kPad; c += kThreads) t.sr[c] = make_float2(1.0f, 1.0f);
+    // codes past the last one, read by work items padded to a whole number
+    // of candidates: a NaN scale gives a NaN SSE, which packs above every
+    // real candidate and so never wins
+    for (uint32_t c = N + threadIdx.x; c < 256u + BfTable::kPad; c += kThreads)
+        t.sr[c] = make_float2(__builtin_nanf(""), __builtin_nanf(""));
     if (threadIdx.x == 0)
         t.fast = SF == SF_E8M0 || (fast_quotient_range(scale_value<SF>(1u) * g) &&
                                    fast_quotient_range(scale_value<SF>(scale_top<SF>()) * g));
@@ -310,11 +314,18 @@ __device__ __forceinline__ void fill_bf_table(BfTable& t, float g) {
 // of the two start codes, so the minimum over the start codes and the window
 // is the exhaustive argmin:
 //  * upper side: an element with a <= T0_c encodes to 0 at scale c and adds
-//    exactly fl(a*a) to the tree, so the tree over {fl(a*a) if a <= T0_c
-//    else 0} is a lower bound of SSE_c (fp32 addition is monotone) that only
-//    grows with c; codes from the first one whose bound exceeds the best are
-//    skipped, and once every element encodes to 0 (a_max <= T0_c) all larger
-//    codes tie with c, so nothing above c can win;
+//    exactly fl(a*a) to the tree.  With scales in the division-free range
+//    (S_c normal, so H_c = S_c / 2 is the exact dequantized value of grid
+//    point 0.5), an element with T0_c < a <= H_c encodes to 0.5 (its
+//    quotient lies in (0.25, 0.5]) and adds exactly fl((H_c - a)^2).  Both
+//    terms only grow with c: (H_c - a)^2 grows with S_c, and where the
+//    element enters the zero bin (a <= T0_c, so S_c < 4a before) it
+//    becomes fl(a*a) >= fl((H_c - a)^2).  So the tree over these terms (0
+//    for every other element) is a lower bound of SSE_c (fp32 addition is
+//    monotone) that only grows with c; codes from the first one whose bound
+//    exceeds the best are skipped, and once every element encodes to 0
+//    (a_max <= T0_c) all larger codes tie with c, so nothing above c can
+//    win;
 //  * lower side: while fl(6 S_c) <= a_max the block maximum saturates and
 //    contributes fl((a_max - fl(6 S_c))^2) <= SSE_c, which shrinks as c
 //    grows; codes below the first one whose term is <= best are skipped.
@@ -365,12 +376,61 @@ __device__ __forceinline__ uint32_t first_true_from(uint32_t lo, uint32_t hi, ui
     return a;
 }
 
+// first_true_from for an answer expected within 2^L - 1 codes above lo: one
+// evaluation at lo + 2^L - 1 confirms that, then L bisection steps with a
+// fixed trip count find it, so the lanes of a wave stay in step.  An answer
+// further up continues with the general search.
+template <int L, class Pred>
+__device__ __forceinline__ uint32_t first_true_up(uint32_t lo, uint32_t hi, Pred pred) {
+    constexpr uint32_t span = (1u << L) - 1u;
+    if (lo >= hi) return hi;
+    uint32_t cap;                         // the answer lies in [lo, cap] (cap == hi: none)
+    if (hi - lo > span) {
+        cap = lo + span;
+        if (!pred(cap)) return first_true_from(cap + 1u, hi, cap + 1u, pred);
+    } else {
+        cap = hi;
+    }
+    uint32_t pos = lo;
+#pragma unroll
+    for (int st = L - 1; st >= 0; --st) {
+        const uint32_t probe = pos + (1u << st) - 1u;
+        if (probe < cap && !pred(probe)) pos += 1u << st;
+    }
+    return pos;
+}
+
+// The mirror image: an answer expected within 2^L - 1 codes below hi.
+template <int L, class Pred>
+__device__ __forceinline__ uint32_t first_true_down(uint32_t lo, uint32_t hi, Pred pred) {
+    constexpr uint32_t span = (1u << L) - 1u;
+    if (lo >= hi) return hi;
+    uint32_t base = lo;                   // the answer lies in [base, hi] (hi: none)
+    if (hi - lo > span) {
+        base = hi - span;
+        if (pred(base - 1u)) return first_true_from(lo, base, base - 1u, pred);
+    }
+    uint32_t pos = base;
+#pragma unroll
+    for (int st = L - 1; st >= 0; --st) {
+        const uint32_t probe = pos + (1u << st) - 1u;
+        if (probe < hi && !pred(probe)) pos += 1u << st;
+    }
+    return pos;
+}
+
 template <int SF, int B, int OFF, bool FAST, int U>
 __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], float a_b, uint32_t c_first,
-                                                        uint32_t c_second, float g, float six_g, const BfTable& t,
-                                                        uint32_t& c_lo, uint32_t& c_hi) {
+                                                        uint32_t c_second, const BfTable& t, uint32_t& c_lo,
+                                                        uint32_t& c_hi) {
     constexpr uint32_t CLO = SF == SF_E8M0 ? 0u : 1u;           // candidate codes [CLO, CEND)
     constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : scale_top<SF>() + 1u;
+    // Window ends are searched within 2^L codes of the start: 4 binades of
+    // an 8-code-per-binade format above, 2 below; E8M0 codes are binades.
+    constexpr int L_UP = SF == SF_E8M0 ? 3 : 5;
+    constexpr int L_DOWN = SF == SF_E8M0 ? 2 : 4;
+    // the half-bin term needs exact halves of the scales (normal S_c)
+    constexpr bool HALF_BIN = FAST;
     // every element encodes to zero at the smallest scale: all codes tie
     if (a_b <= t.t0[CLO]) {
         c_lo = c_hi = CLO;
@@ -387,41 +447,46 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
     const float best0 = as_f((uint32_t)(best >> 32));
     const uint32_t c_best = (uint32_t)(best & 0xFFFFFFFFull);
 
-    // fl(6 S_c), computed the way the encoder computes it (grid value 6 times S_c)
-    auto six_s = [&](uint32_t c) {
-        if constexpr (SF == SF_E8M0) return 6.0f * e8m0_value(c);
-        else return 6.0f * (scale_value<SF>(c) * g);
-    };
-
-    // upper end: first code past c_best whose zero-bin bound exceeds best0, or
-    // whose every element encodes to zero (that code is still evaluated)
-    float sq[B];
+    // upper end: first code past c_best whose bound exceeds best0, or whose
+    // every element encodes to zero (that code is still evaluated)
+    float a[B], sq[B];
 #pragma unroll
-    for (int i = 0; i < B; ++i) sq[i] = y[OFF + i] * y[OFF + i];
+    for (int i = 0; i < B; ++i) {
+        a[i] = fabsf(y[OFF + i]);
+        sq[i] = a[i] * a[i];
+    }
     auto stop_up = [&](uint32_t c) {
         const float T0 = t.t0[c];
         float z[B];
+        if constexpr (HALF_BIN) {
+            // min(fl(max(H - a, 0)^2), fl(a^2)) per element: the exact term
+            // of the lower half of the 0.5 bin, of the zero bin (there
+            // a <= S/4, so the second square is the smaller, except in the
+            // rounding sliver just above S/4 where the first one is still a
+            // lower bound), and 0 above H.  It grows with S_c, so the bound
+            // keeps its monotonicity without a bin test.
+            const float H = 0.5f * t.sr[c].x;
 #pragma unroll
-        for (int i = 0; i < B; ++i) z[i] = fabsf(y[OFF + i]) <= T0 ? sq[i] : 0.0f;
+            for (int i = 0; i < B; ++i) {
+                const float d = fmaxf(H - a[i], 0.0f);
+                z[i] = fminf(d * d, sq[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B; ++i) z[i] = a[i] <= T0 ? sq[i] : 0.0f;
+        }
         return tree_sum<B>(z) > best0 || a_b <= T0;
     };
-    uint32_t guess_hi;
-    if constexpr (SF == SF_E8M0) guess_hi = c_best + 3u;
-    else guess_hi = scale_encode<SF>(a_b / g) + 16u;      // around where a_max / S drops near 0.25 * 4
-    c_hi = first_true_from(c_best + 1u, CEND, guess_hi, stop_up);
+    c_hi = first_true_up<L_UP>(c_best + 1u, CEND, stop_up);
     if (c_hi < CEND && a_b <= t.t0[c_hi]) ++c_hi;
 
     // lower end: below c_star the block maximum saturates (fl(6 S) <= a_max) and
     // contributes (a_max - fl(6 S))^2; skip the codes where that exceeds best0
-    const uint32_t c_star = first_true_from(CLO, CEND, c_first, [&](uint32_t c) { return six_s(c) > a_b; });
-    auto keep_lo = [&](uint32_t c) {
-        const float d = a_b - six_s(c);
+    const uint32_t c_star = first_true_from(CLO, CEND, c_first, [&](uint32_t c) { return t.six[c] > a_b; });
+    c_lo = first_true_down<L_DOWN>(CLO, c_star, [&](uint32_t c) {
+        const float d = a_b - t.six[c];
         return d * d <= best0;
-    };
-    uint32_t guess_lo;
-    if constexpr (SF == SF_E8M0) guess_lo = c_star > CLO ? c_star - 1u : CLO;
-    else guess_lo = scale_encode<SF>(fmaxf(a_b - __builtin_sqrtf(best0), 0.0f) / six_g);
-    c_lo = first_true_from(CLO, c_star, guess_lo, keep_lo);
+    });
     return best;
 }
 
@@ -877,7 +942,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
         unsigned long long best[NBLK];
         uint32_t start[NBLK + 1];
         uint8_t clo[NBLK];
-        uint8_t chi[NBLK];
     };
     __shared__ __attribute__((aligned(16))) WaveLds s_w[kThreads / 64];
     __shared__ BfTable s_bf;
@@ -888,7 +952,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
 
     const float g = workgroup_global_scale(p);
     if (blockIdx.x == 0 && threadIdx.x == 0 && p.g_out) *p.g_out = g;
-    const float six_g = 6.0f * g, four_g = 4.0f * g;
+    // start codes only need to be near the abs-max and map-to-4 scales (any
+    // start gives the same result), so reciprocals replace the divisions
+    const float inv_six_g = 1.0f / (6.0f * g), inv_four_g = 1.0f / (4.0f * g);
     fill_bf_table<SF>(s_bf, g);
     const bool fast = s_bf.fast;
 
@@ -940,13 +1006,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                     c1 = e8m0_absmax_code(ab);
                     c2 = c1 < 254u ? c1 + 1u : c1;
                 } else {
-                    const uint32_t s6 = scale_encode<SF>(a_b / six_g), s4 = scale_encode<SF>(a_b / four_g);
+                    const uint32_t s6 = scale_encode<SF>(a_b * inv_six_g), s4 = scale_encode<SF>(a_b * inv_four_g);
                     c1 = s6 > 0u ? s6 : 1u;
                     c2 = s4 > 0u ? s4 : 1u;
                 }
                 uint32_t lo, hi;
-                if (fast) best = bf_window<SF, B, b * B, true>(y, a_b, c1, c2, g, six_g, s_bf, lo, hi);
-                else best = bf_window<SF, B, b * B, false>(y, a_b, c1, c2, g, six_g, s_bf, lo, hi);
+                if (fast) best = bf_window<SF, B, b * B, true>(y, a_b, c1, c2, s_bf, lo, hi);
+                else best = bf_window<SF, B, b * B, false>(y, a_b, c1, c2, s_bf, lo, hi);
                 clo[b] = lo;
                 chi[b] = hi;
                 n[b] = hi > lo ? (hi - lo + K - 1) / K : 0u;     // work items of K codes
@@ -965,7 +1031,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
         for (int b = 0; b < NB; ++b) {
             W.start[lane * NB + b] = run;
             W.clo[lane * NB + b] = (uint8_t)clo[b];
-            W.chi[lane * NB + b] = (uint8_t)chi[b];
             run += n[b];
         }
         if (lane == 63) W.start[NBLK] = total;
@@ -991,7 +1056,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             };
             float yb[B];
             load_block(k, yb);
-            uint32_t k_begin = W.start[k], k_end = W.start[k + 1], k_clo = W.clo[k], k_chi = W.chi[k];
+            uint32_t k_begin = W.start[k], k_end = W.start[k + 1], k_clo = W.clo[k];
             unsigned long long local = ~0ull;
 #pragma unroll 1
             for (uint32_t j = j0; j < j1; ++j) {
@@ -1002,11 +1067,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                     k_begin = k_end;
                     k_end = W.start[k + 1];
                     k_clo = W.clo[k];
-                    k_chi = W.chi[k];
                     if (j < k_end) load_block(k, yb);
                 }
-                // K consecutive codes of block k; codes past the window are evaluated
-                // (the table is padded) and discarded
+                // K consecutive codes of block k.  The last item of a window may run
+                // past its end: those codes are real candidates (more candidates
+                // cannot change the argmin) or table padding (NaN SSE)
                 const uint32_t c0 = k_clo + K * (j - k_begin);
                 float2 es[K];
 #pragma unroll
@@ -1019,7 +1084,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
                     float sse;
                     if (fast) sse = encode_block<SF, B, 0, false, true>(yb, e.x, e.y, rc);
                     else sse = encode_block<SF, B, 0, false, false>(yb, e.x, e.y, rc);
-                    const unsigned long long cand = (q == 0 || c < k_chi) ? pack_candidate(sse, c) : ~0ull;
+                    const unsigned long long cand = pack_candidate(sse, c);
                     local = cand < local ? cand : local;
                 }
             }

@@ -90,6 +90,23 @@ def test_e8m0_block_sizes(O_lib, strategy, B):
     compare_quant(gpu_quantize(x, S.F32, cfg), oracle_quantize(x, S.F32, cfg))
 
 
+@pytest.mark.parametrize("fmt,B,gm", [(E4M3, 4, NONE), (E4M3, 4, TAMAX), (E4M3, 8, NONE), (E4M3, 8, TAMAX),
+                                      (E4M3, 16, NONE), (E4M3, 16, TAMAX), (E4M3, 32, NONE), (E4M3, 32, TAMAX),
+                                      (E8M0, 16, NONE), (E8M0, 32, NONE), (F.UE5M3, 16, NONE)])
+@pytest.mark.parametrize("kind", ["normal", "laplace"])
+def test_brute_force_many_blocks(O_lib, fmt, B, gm, kind):
+    """Brute force on 64 x 4096 values (8192 to 65536 blocks per case), every
+    block against the oracle's exhaustive search: the branch-and-bound
+    windows must never cut off the argmin."""
+    x = S.normal(64, 4096, 21) if kind == "normal" else S.laplace(64, 4096, 22)
+    cfg = F.config(fmt, B, BF, gm)
+    note(f"brute force many blocks fmt={fmt} B={B} gm={gm} {kind}")
+    gpu = gpu_quantize(x, S.F32, cfg, dq_dt=None)
+    ref = oracle_quantize(x, S.F32, cfg, dq_dt=None)
+    assert gpu["g"].view(np.uint32) == ref["g"].view(np.uint32)
+    compare_quant(gpu, ref, keys=("scales", "codes", "mse"))
+
+
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("strategy", [ABSMAX, PZ, FOS, BF])
 def test_block_sweep_full_size_sampled(O_lib, kind, strategy):
