@@ -235,6 +235,44 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// Streaming stores for the outputs that are written once, never read back
+// by the kernel, and large next to its input: dequantized tensors (as large
+// as the input) and per-block errors.  Non-temporal, so they do not evict
+// the input tensors from L2 and the last-level cache.  Only for stores
+// where a wave writes whole contiguous lines (partial-line non-temporal
+// writes are slow).  Codes and scales, which the next operation
+// (dequantize, GEMM) reads, are stored normally.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+    u32x4_t w;
+    w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream(uint2* p, uint2 v) {
+    u32x2_t w;
+    w.x = v.x; w.y = v.y;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void store_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
+// N consecutive fp32 values (N = 1, 2, 4 or 8; p aligned to 4 N bytes) as
+// streaming stores, so that lanes writing neighbouring runs fill whole lines.
+template <int N>
+__device__ __forceinline__ void store_stream_f32(float* p, const float (&v)[N]) {
+    if constexpr (N == 1) {
+        store_stream(p, v[0]);
+    } else if constexpr (N == 2) {
+        store_stream(reinterpret_cast<uint2*>(p), make_uint2(as_u(v[0]), as_u(v[1])));
+    } else {
+        static_assert(N % 4 == 0, "runs of 1, 2 or a multiple of 4 values");
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i)
+            store_stream(reinterpret_cast<uint4*>(p) + i,
+                         make_uint4(as_u(v[4 * i]), as_u(v[4 * i + 1]), as_u(v[4 * i + 2]), as_u(v[4 * i + 3])));
+    }
+}
+
 // Store N fp32 values as dtype dt at base + off (elements); N * size is a
 // multiple of 8 bytes and the address is aligned to that.
 template <int N>

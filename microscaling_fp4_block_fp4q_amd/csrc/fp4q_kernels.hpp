@@ -629,7 +629,8 @@ __device__ __forceinline__ void tile_load(const T* __restrict__ base, int nvalid
 }
 
 // Copy a tile of nvalid units whose values (type of size EO) sit in the
-// lanes' LDS slots to out_base, 16 coalesced bytes per lane.
+// lanes' LDS slots to out_base, 16 coalesced bytes per lane, as streaming
+// stores.
 template <int U, int EO>
 __device__ __forceinline__ void tile_flush_t(void* __restrict__ out_base, int nvalid, const char* lds, int lane) {
     constexpr int UB = U * EO;                 // bytes of one unit
@@ -642,7 +643,7 @@ __device__ __forceinline__ void tile_flush_t(void* __restrict__ out_base, int nv
 #pragma unroll
         for (int k = 0; k < C; ++k) {
             const int j = k * 64 + lane;
-            if (j < nchunks) dst[j] = *reinterpret_cast<const uint4*>(lds + (j / C) * SLOT + (j % C) * 16);
+            if (j < nchunks) store_stream(dst + j, *reinterpret_cast<const uint4*>(lds + (j / C) * SLOT + (j % C) * 16));
         }
     } else {
         static_assert(UB == 8, "units of 4 two-byte values");
@@ -650,10 +651,10 @@ __device__ __forceinline__ void tile_flush_t(void* __restrict__ out_base, int nv
         if (lane < nchunks) {
             const uint2 a = *reinterpret_cast<const uint2*>(lds + (2 * lane) * SLOT);
             const uint2 b = *reinterpret_cast<const uint2*>(lds + (2 * lane + 1) * SLOT);
-            dst[lane] = make_uint4(a.x, a.y, b.x, b.y);
+            store_stream(dst + lane, make_uint4(a.x, a.y, b.x, b.y));
         }
         if ((nvalid & 1) && lane == nvalid - 1)
-            reinterpret_cast<uint2*>(out_base)[lane] = *reinterpret_cast<const uint2*>(lds + lane * SLOT);
+            store_stream(reinterpret_cast<uint2*>(out_base) + lane, *reinterpret_cast<const uint2*>(lds + lane * SLOT));
     }
     wave_sync_lds();
 }
@@ -888,16 +889,15 @@ __device__ __forceinline__ void store_unit_outputs(const QuantArgs& p, int64_t u
 #pragma unroll
             for (int b = 0; b < NB; ++b) p.scales[u * NB + b] = (uint8_t)sc[b];
         }
-        if (p.sse) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) p.sse[u * NB + b] = sse[b];
-        }
+        if (p.sse) store_stream_f32<NB>(p.sse + u * NB, sse);
         if (p.mse) {
+            float m[NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const float m = sse[b] * (1.0f / (float)B);   // exact: B is a power of two
-                p.mse[u * NB + b] = (m == m) ? m : as_f(kQNaN);
+                const float v = sse[b] * (1.0f / (float)B);   // exact: B is a power of two
+                m[b] = (v == v) ? v : as_f(kQNaN);
             }
+            store_stream_f32<NB>(p.mse + u * NB, m);
         }
     }
     if (p.dq && p.contiguous) {
@@ -1195,6 +1195,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MseArgs p) {
         if constexpr (H > 0) fwht_segments<H, U>(y);
         uint32_t c[U];
         load_codes<U>(p.codes + u * (U / 2), c);
+        float mse[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             bool usable;
@@ -1209,8 +1210,9 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MseArgs p) {
                 e[i] = d * d;
             }
             const float m = tree_sum<B>(e) * (1.0f / (float)B);
-            p.mse[u * NB + b] = (nan_block || m != m) ? as_f(kQNaN) : m;
+            mse[b] = (nan_block || m != m) ? as_f(kQNaN) : m;
         }
+        store_stream_f32<NB>(p.mse + u * NB, mse);
     }
 }
 
