@@ -637,7 +637,8 @@ def main():
     else:
         search = time_quantize_configs(F, torch, X["normal"], [
             ("absmax", F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_SEARCH)),
-            ("4-over-6", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_SEARCH))])
+            ("4-over-6", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_SEARCH)),
+            ("brute-force", F.config(F.E4M3, 16, F.BRUTE_FORCE, F.GLOBAL_SEARCH))])
         ue5m3 = time_quantize_configs(F, torch, X["normal"], [
             (f"B={B} {STRATS[st]}", F.config(F.UE5M3, B, st)) for B in (16, 4) for st in (0, 2, 3)])
         hist = time_histogram(F, torch, X["normal"])

@@ -59,13 +59,13 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 3
+#define FP4Q_ABI_VERSION 4
 
 typedef enum {
     FP4Q_OK = 0,
     FP4Q_ERR_INVALID_ARG = 1, /* null required pointer, bad enum, bad user scale */
     FP4Q_ERR_UNSUPPORTED = 2, /* combination the formats do not define, or SEARCH
-                                 with BRUTE_FORCE or GIVEN */
+                                 with GIVEN */
     FP4Q_ERR_SHAPE = 3,       /* block / rotation / sub-block does not tile the row */
     FP4Q_ERR_ALIGNMENT = 4,   /* base pointer or row pitch not 16-byte aligned */
     FP4Q_ERR_DEVICE = 5       /* the HIP runtime refused a launch */
@@ -109,7 +109,9 @@ typedef enum {
  * j = 0..31, are each scored by the fp64 balanced-tree sum, over all blocks
  * in row-major order (zero-padded to a power of two), of the fp32 block SSE
  * under the configured strategy; the smallest total wins, ties to the
- * smallest j.  Strategies ABSMAX, PREVENT_ZERO and FOUR_OVER_SIX. */
+ * smallest j.  Strategies ABSMAX, PREVENT_ZERO, FOUR_OVER_SIX and
+ * BRUTE_FORCE (each block at its exhaustive-argmin scale for every
+ * candidate: 32 brute-force searches of the tensor). */
 typedef enum {
     FP4Q_GLOBAL_NONE = 0,
     FP4Q_GLOBAL_TENSOR_AMAX = 1,

@@ -43,9 +43,7 @@ fp4q_status check_config(const fp4q_config* cfg) {
     if (cfg->scale_fmt == FP4Q_SCALE_UE5M3 &&
         (cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX || cfg->global_mode == FP4Q_GLOBAL_SEARCH))
         return FP4Q_ERR_UNSUPPORTED;
-    if (cfg->global_mode == FP4Q_GLOBAL_SEARCH &&
-        (cfg->strategy == FP4Q_BRUTE_FORCE || cfg->strategy == FP4Q_GIVEN))
-        return FP4Q_ERR_UNSUPPORTED;
+    if (cfg->global_mode == FP4Q_GLOBAL_SEARCH && cfg->strategy == FP4Q_GIVEN) return FP4Q_ERR_UNSUPPORTED;
     if (cfg->global_mode == FP4Q_GLOBAL_USER) {
         const double g = cfg->global_scale;
         if (!(g >= FLT_MIN) || !(448.0 * g < FLT_MAX)) return FP4Q_ERR_INVALID_ARG;
@@ -158,7 +156,9 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
         double* level0 = reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) + kAmaxBytes);
         double* level1 = level0 + (size_t)kSearchCandidates * ga.ntiles;
         ga.partials = level0;
-        const int st = cfg->strategy == FP4Q_FOUR_OVER_SIX ? ST_FOUR_OVER_SIX : ST_ABSMAX;
+        const int st = cfg->strategy == FP4Q_FOUR_OVER_SIX ? ST_FOUR_OVER_SIX
+                       : cfg->strategy == FP4Q_BRUTE_FORCE ? ST_BRUTE_FORCE
+                                                           : ST_ABSMAX;
         const int grid = grid_for(ga.units);
         hipError_t e;
         switch (x_dt) {

@@ -916,20 +916,36 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
     return v;
 }
 
-// Brute-force quantize (exhaustive argmin, computed as branch and bound).
-// Per tile: each lane publishes its (rotated) fp32 values in LDS and finds,
+// LDS of one wave of the brute-force kernels: the tile's fp32 values (one
+// padded slot per lane), each block's best candidate, and the work list.
+template <int U, int B>
+struct BfWaveLds {
+    static constexpr int NBLK = kTileUnits * (U / B);
+    char tile[kTileUnits * slot_bytes<U>()];
+    unsigned long long best[NBLK];
+    uint32_t start[NBLK + 1];
+    uint8_t clo[NBLK];
+};
+
+// Brute-force search of one tile (exhaustive argmin, computed as branch and
+// bound).  Each lane publishes its (rotated) fp32 values y in LDS and finds,
 // for each of its blocks, the best of two start scales and the window of
 // codes that can still beat it (bf_window).  The windows of all blocks of the
 // tile form one work list that the 64 lanes split evenly: a work item is K
 // consecutive codes of one block (K = 16 / B for small blocks, which gives a
 // lane independent candidates to interleave; a window is padded to whole
-// items and the padding discarded).  A lane walks its slice, evaluates the
-// items with the block's values read from LDS, and merges its per-block
-// minimum into an LDS 64-bit atomic minimum over (SSE bits, code).  Then
-// every lane encodes its blocks at the winning code.
-template <class InT, int B, int H, int SF>
-__global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
-    constexpr int U = unit_elems<InT, B, H>();
+// items).  A lane walks its slice, evaluates the items with the block's
+// values read from LDS, and merges its per-block minimum into an LDS 64-bit
+// atomic minimum over (SSE bits, code).  On return W.best[lane * NB + b]
+// holds the winning code of each finite block in its low word (its high
+// word is the SSE the search saw, 0 for a block whose elements all encode
+// to zero at every scale), and nan_blk[b] flags blocks with a NaN or
+// infinite value or a non-finite g.  Idle lanes (active false) must hold
+// zeros in y.
+template <int SF, int B, int U>
+__device__ __forceinline__ void bf_search_tile(const float (&y)[U], bool active, float g, float inv_six_g,
+                                               float inv_four_g, const BfTable& s_bf, BfWaveLds<U, B>& W, int lane,
+                                               bool (&nan_blk)[U / B]) {
     constexpr int NB = U / B;
     constexpr int SLOT = slot_bytes<U>();
     constexpr int NBLK = kTileUnits * NB;
@@ -937,18 +953,167 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
     constexpr int K = B >= 16 ? 1 : 16 / B;       // candidates of one block per work item
     // an item reads codes c0 .. c0 + K - 1 with c0 < CEND
     static_assert(CEND + K - 1 <= 256 + BfTable::kPad, "items read past the table");
-    struct WaveLds {
-        char tile[kTileUnits * SLOT];
-        unsigned long long best[NBLK];
-        uint32_t start[NBLK + 1];
-        uint8_t clo[NBLK];
-    };
-    __shared__ __attribute__((aligned(16))) WaveLds s_w[kThreads / 64];
+    const bool fast = s_bf.fast;
+
+    // publish the fp32 values of this lane's unit
+#pragma unroll
+    for (int i = 0; i < U / 4; ++i)
+        reinterpret_cast<float4*>(W.tile + lane * SLOT)[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+
+    // start candidates and windows of this lane's blocks
+    uint32_t n[NB], clo[NB];
+    static_for<NB>([&](auto bi) {
+        constexpr int b = decltype(bi)::value;
+        uint32_t ab = 0;
+#pragma unroll
+        for (int i = 0; i < B; ++i) ab = max(ab, as_u(y[b * B + i]) & 0x7FFFFFFFu);
+        nan_blk[b] = ab >= 0x7F800000u || !(g < __builtin_inff());
+        n[b] = 0;
+        clo[b] = 0;
+        unsigned long long best = ~0ull;
+        if (!nan_blk[b] && active) {
+            const float a_b = as_f(ab);
+            uint32_t c1, c2;
+            if constexpr (SF == SF_E8M0) {
+                c1 = e8m0_absmax_code(ab);
+                c2 = c1 < 254u ? c1 + 1u : c1;
+            } else {
+                const uint32_t s6 = scale_encode<SF>(a_b * inv_six_g), s4 = scale_encode<SF>(a_b * inv_four_g);
+                c1 = s6 > 0u ? s6 : 1u;
+                c2 = s4 > 0u ? s4 : 1u;
+            }
+            uint32_t lo, hi;
+            if (fast) best = bf_window<SF, B, b * B, true>(y, a_b, c1, c2, s_bf, lo, hi);
+            else best = bf_window<SF, B, b * B, false>(y, a_b, c1, c2, s_bf, lo, hi);
+            clo[b] = lo;
+            n[b] = hi > lo ? (hi - lo + K - 1) / K : 0u;     // work items of K codes
+        }
+        W.best[lane * NB + b] = best;
+    });
+
+    // one work list for the tile
+    uint32_t mine = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mine += n[b];
+    const uint32_t incl = wave_inclusive_sum(mine, lane);
+    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+    uint32_t run = incl - mine;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        W.start[lane * NB + b] = run;
+        W.clo[lane * NB + b] = (uint8_t)clo[b];
+        run += n[b];
+    }
+    if (lane == 63) W.start[NBLK] = total;
+    wave_sync_lds();
+
+    const uint32_t j0 = (uint32_t)(((uint64_t)total * lane) >> 6);
+    const uint32_t j1 = (uint32_t)(((uint64_t)total * (lane + 1)) >> 6);
+    if (j0 < j1) {
+        // block k containing item j0: the largest k with start[k] <= j0
+        uint32_t lo = 0, hi = NBLK;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if (W.start[mid] <= j0) lo = mid; else hi = mid - 1;
+        }
+        uint32_t k = lo;
+        auto load_block = [&](uint32_t kk, float (&dst)[B]) {
+            const float4* src = reinterpret_cast<const float4*>(W.tile + (kk / NB) * SLOT + (kk % NB) * B * 4);
+#pragma unroll
+            for (int i = 0; i < B / 4; ++i) {
+                const float4 v = src[i];
+                dst[4 * i] = v.x; dst[4 * i + 1] = v.y; dst[4 * i + 2] = v.z; dst[4 * i + 3] = v.w;
+            }
+        };
+        float yb[B];
+        load_block(k, yb);
+        uint32_t k_begin = W.start[k], k_end = W.start[k + 1], k_clo = W.clo[k];
+        unsigned long long local = ~0ull;
+#pragma unroll 1
+        for (uint32_t j = j0; j < j1; ++j) {
+            while (j >= k_end) {
+                atomicMin(&W.best[k], local);
+                local = ~0ull;
+                ++k;
+                k_begin = k_end;
+                k_end = W.start[k + 1];
+                k_clo = W.clo[k];
+                if (j < k_end) load_block(k, yb);
+            }
+            // K consecutive codes of block k.  The last item of a window may run
+            // past its end: those codes are real candidates (more candidates
+            // cannot change the argmin) or table padding (NaN SSE)
+            const uint32_t c0 = k_clo + K * (j - k_begin);
+            float2 es[K];
+#pragma unroll
+            for (int q = 0; q < K; ++q) es[q] = s_bf.sr[c0 + q];
+#pragma unroll
+            for (int q = 0; q < K; ++q) {
+                const uint32_t c = c0 + q;
+                const float2 e = es[q];
+                float rc[B];
+                float sse;
+                if (fast) sse = encode_block<SF, B, 0, false, true>(yb, e.x, e.y, rc);
+                else sse = encode_block<SF, B, 0, false, false>(yb, e.x, e.y, rc);
+                const unsigned long long cand = pack_candidate(sse, c);
+                local = cand < local ? cand : local;
+            }
+        }
+        atomicMin(&W.best[k], local);
+    }
+    wave_sync_lds();
+}
+
+// SSE of block BI of a unit at the winning code c of a brute-force search,
+// computed as the quantizer computes it (r receives the grid values).
+template <int SF, int B, int BI, int U>
+__device__ __forceinline__ float bf_block_sse(const float (&y)[U], uint32_t c, const BfTable& s_bf, float (&r)[B],
+                                              float& S) {
+    constexpr int OFF = BI * B;
+    if constexpr (SF == SF_E8M0) {
+        S = e8m0_value(c);
+        return encode_block<SF, B, OFF, false, true>(y, S, e8m0_inverse(c), r);
+    } else {
+        S = s_bf.sr[c].x;
+        return encode_block_at<B, OFF, false>(y, S, r);
+    }
+}
+
+// Tile load for the brute-force kernels: contiguous tensors through the
+// wave's LDS slots, strided ones unit by unit; rotated when H != 0; idle
+// lanes hold zeros (they contribute empty windows).
+template <class InT, int U, int H, class P>
+__device__ __forceinline__ void bf_load_tile(const P& p, int64_t u0, int nvalid, int lane, char* lds, float (&y)[U]) {
+    const InT* x = reinterpret_cast<const InT*>(p.x);
+    const int64_t u = u0 + lane;
+    const bool active = lane < nvalid;
+    if (p.contiguous) {
+        tile_load<InT, U>(x + u0 * U, nvalid, lds, lane, y);
+    } else if (active) {
+        load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, false), y);
+    } else {
+#pragma unroll
+        for (int i = 0; i < U; ++i) y[i] = 0.0f;
+    }
+    if constexpr (H > 0) fwht_segments<H, U>(y);
+    if (!active) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) y[i] = 0.0f;
+    }
+}
+
+// Brute-force quantize: bf_search_tile per tile, then every lane encodes its
+// blocks at the winning codes and stores the outputs.
+template <class InT, int B, int H, int SF>
+__global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
+    constexpr int U = unit_elems<InT, B, H>();
+    constexpr int NB = U / B;
+    constexpr uint32_t CEND = SF == SF_E8M0 ? 255u : scale_top<SF>() + 1u;
+    __shared__ __attribute__((aligned(16))) BfWaveLds<U, B> s_w[kThreads / 64];
     __shared__ BfTable s_bf;
 
-    const InT* x = reinterpret_cast<const InT*>(p.x);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    WaveLds& W = s_w[wave];
+    BfWaveLds<U, B>& W = s_w[wave];
 
     const float g = workgroup_global_scale(p);
     if (blockIdx.x == 0 && threadIdx.x == 0 && p.g_out) *p.g_out = g;
@@ -956,7 +1121,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
     // start gives the same result), so reciprocals replace the divisions
     const float inv_six_g = 1.0f / (6.0f * g), inv_four_g = 1.0f / (4.0f * g);
     fill_bf_table<SF>(s_bf, g);
-    const bool fast = s_bf.fast;
 
     const int64_t ntiles = (p.units + kTileUnits - 1) / kTileUnits;
     const int64_t tstride = (int64_t)gridDim.x * (kThreads / 64);
@@ -967,130 +1131,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
         const bool active = lane < nvalid;
 
         float y[U];
-        if (p.contiguous) {
-            tile_load<InT, U>(x + u0 * U, nvalid, W.tile, lane, y);
-        } else if (active) {
-            load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, false), y);
-        } else {
-#pragma unroll
-            for (int i = 0; i < U; ++i) y[i] = 0.0f;
-        }
-        if constexpr (H > 0) fwht_segments<H, U>(y);
-        if (!active) {
-#pragma unroll
-            for (int i = 0; i < U; ++i) y[i] = 0.0f;     // idle lanes contribute empty windows
-        }
-
-        // publish the fp32 values of this lane's unit
-#pragma unroll
-        for (int i = 0; i < U / 4; ++i)
-            reinterpret_cast<float4*>(W.tile + lane * SLOT)[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
-
-        // start candidates and windows of this lane's blocks
-        uint32_t n[NB], clo[NB], chi[NB];
+        bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
         bool nan_blk[NB];
-        static_for<NB>([&](auto bi) {
-            constexpr int b = decltype(bi)::value;
-            uint32_t ab = 0;
-#pragma unroll
-            for (int i = 0; i < B; ++i) ab = max(ab, as_u(y[b * B + i]) & 0x7FFFFFFFu);
-            nan_blk[b] = ab >= 0x7F800000u || !(g < __builtin_inff());
-            n[b] = 0;
-            clo[b] = 0;
-            chi[b] = 0;
-            unsigned long long best = ~0ull;
-            if (!nan_blk[b] && active) {
-                const float a_b = as_f(ab);
-                uint32_t c1, c2;
-                if constexpr (SF == SF_E8M0) {
-                    c1 = e8m0_absmax_code(ab);
-                    c2 = c1 < 254u ? c1 + 1u : c1;
-                } else {
-                    const uint32_t s6 = scale_encode<SF>(a_b * inv_six_g), s4 = scale_encode<SF>(a_b * inv_four_g);
-                    c1 = s6 > 0u ? s6 : 1u;
-                    c2 = s4 > 0u ? s4 : 1u;
-                }
-                uint32_t lo, hi;
-                if (fast) best = bf_window<SF, B, b * B, true>(y, a_b, c1, c2, s_bf, lo, hi);
-                else best = bf_window<SF, B, b * B, false>(y, a_b, c1, c2, s_bf, lo, hi);
-                clo[b] = lo;
-                chi[b] = hi;
-                n[b] = hi > lo ? (hi - lo + K - 1) / K : 0u;     // work items of K codes
-            }
-            W.best[lane * NB + b] = best;
-        });
-
-        // one work list for the tile
-        uint32_t mine = 0;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) mine += n[b];
-        const uint32_t incl = wave_inclusive_sum(mine, lane);
-        const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-        uint32_t run = incl - mine;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            W.start[lane * NB + b] = run;
-            W.clo[lane * NB + b] = (uint8_t)clo[b];
-            run += n[b];
-        }
-        if (lane == 63) W.start[NBLK] = total;
-        wave_sync_lds();
-
-        const uint32_t j0 = (uint32_t)(((uint64_t)total * lane) >> 6);
-        const uint32_t j1 = (uint32_t)(((uint64_t)total * (lane + 1)) >> 6);
-        if (j0 < j1) {
-            // block k containing item j0: the largest k with start[k] <= j0
-            uint32_t lo = 0, hi = NBLK;
-            while (lo < hi) {
-                const uint32_t mid = (lo + hi + 1) >> 1;
-                if (W.start[mid] <= j0) lo = mid; else hi = mid - 1;
-            }
-            uint32_t k = lo;
-            auto load_block = [&](uint32_t kk, float (&dst)[B]) {
-                const float4* src = reinterpret_cast<const float4*>(W.tile + (kk / NB) * SLOT + (kk % NB) * B * 4);
-#pragma unroll
-                for (int i = 0; i < B / 4; ++i) {
-                    const float4 v = src[i];
-                    dst[4 * i] = v.x; dst[4 * i + 1] = v.y; dst[4 * i + 2] = v.z; dst[4 * i + 3] = v.w;
-                }
-            };
-            float yb[B];
-            load_block(k, yb);
-            uint32_t k_begin = W.start[k], k_end = W.start[k + 1], k_clo = W.clo[k];
-            unsigned long long local = ~0ull;
-#pragma unroll 1
-            for (uint32_t j = j0; j < j1; ++j) {
-                while (j >= k_end) {
-                    atomicMin(&W.best[k], local);
-                    local = ~0ull;
-                    ++k;
-                    k_begin = k_end;
-                    k_end = W.start[k + 1];
-                    k_clo = W.clo[k];
-                    if (j < k_end) load_block(k, yb);
-                }
-                // K consecutive codes of block k.  The last item of a window may run
-                // past its end: those codes are real candidates (more candidates
-                // cannot change the argmin) or table padding (NaN SSE)
-                const uint32_t c0 = k_clo + K * (j - k_begin);
-                float2 es[K];
-#pragma unroll
-                for (int q = 0; q < K; ++q) es[q] = s_bf.sr[c0 + q];
-#pragma unroll
-                for (int q = 0; q < K; ++q) {
-                    const uint32_t c = c0 + q;
-                    const float2 e = es[q];
-                    float rc[B];
-                    float sse;
-                    if (fast) sse = encode_block<SF, B, 0, false, true>(yb, e.x, e.y, rc);
-                    else sse = encode_block<SF, B, 0, false, false>(yb, e.x, e.y, rc);
-                    const unsigned long long cand = pack_candidate(sse, c);
-                    local = cand < local ? cand : local;
-                }
-            }
-            atomicMin(&W.best[k], local);
-        }
-        wave_sync_lds();
+        bf_search_tile<SF, B, U>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
 
         // encode every block at its winning code
         uint32_t cw[code_words(U)];
@@ -1101,7 +1144,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
         float sse[NB];
         static_for<NB>([&](auto bi) {
             constexpr int b = decltype(bi)::value;
-            constexpr int OFF = b * B;
             float r[B];
             float S = 0.0f;
             if (nan_blk[b]) {
@@ -1112,17 +1154,59 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             } else {
                 const uint32_t c = (uint32_t)(W.best[lane * NB + b] & 0xFFFFFFFFull) % CEND;
                 sc[b] = c;
-                if constexpr (SF == SF_E8M0) {
-                    S = e8m0_value(c);
-                    sse[b] = encode_block<SF, B, OFF, false, true>(y, S, e8m0_inverse(c), r);
-                } else {
-                    S = s_bf.sr[c].x;
-                    sse[b] = encode_block_at<B, OFF, false>(y, S, r);
-                }
+                sse[b] = bf_block_sse<SF, B, b>(y, c, s_bf, r, S);
             }
-            finish_block<B, OFF>(y, r, S, nan_blk[b], cw, sink);
+            finish_block<B, b * B>(y, r, S, nan_blk[b], cw, sink);
         });
         store_unit_outputs<B, U>(p, u0, nvalid, lane, W.tile, cw, sc, sse, true);
+    }
+}
+
+// Per-tensor scale search with the brute-force block search inside: for each
+// candidate g_j (one table fill per candidate, shared by the workgroup) every
+// tile runs bf_search_tile and scores its blocks at their winning codes; the
+// per-tile fp64 sums go to the same partials as k_gsearch.
+template <class InT, int B, int H>
+__global__ __launch_bounds__(kThreads) void k_gsearch_bf(GSearchArgs p) {
+    constexpr int U = unit_elems<InT, B, H>();
+    constexpr int NB = U / B;
+    constexpr uint32_t CEND = scale_top<SF_E4M3>() + 1u;
+    __shared__ __attribute__((aligned(16))) BfWaveLds<U, B> s_w[kThreads / 64];
+    __shared__ BfTable s_bf;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    BfWaveLds<U, B>& W = s_w[wave];
+    const float g0 = workgroup_amax_scale(p.amax_partials, p.n_partials);
+
+    const int64_t ntiles = (p.units + kTileUnits - 1) / kTileUnits;
+    const int64_t tstride = (int64_t)gridDim.x * (kThreads / 64);
+#pragma unroll 1
+    for (int j = 0; j < kSearchCandidates; ++j) {
+        const float g = g0 * search_factor(j);
+        const float inv_six_g = 1.0f / (6.0f * g), inv_four_g = 1.0f / (4.0f * g);
+        fill_bf_table<SF_E4M3>(s_bf, g);
+        for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < ntiles; t += tstride) {
+            const int64_t u0 = t * kTileUnits;
+            const int nvalid = (int)min<int64_t>(kTileUnits, p.units - u0);
+            const bool active = lane < nvalid;
+            float y[U];
+            bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
+            bool nan_blk[NB];
+            bf_search_tile<SF_E4M3, B, U>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            double e[NB];
+            static_for<NB>([&](auto bi) {
+                constexpr int b = decltype(bi)::value;
+                float r[B], S;
+                const uint32_t c = (uint32_t)(W.best[lane * NB + b] & 0xFFFFFFFFull) % CEND;
+                e[b] = nan_blk[b] ? (double)as_f(kQNaN) : (double)bf_block_sse<SF_E4M3, B, b>(y, c, s_bf, r, S);
+            });
+            double s = active ? tree_sum<NB>(e) : 0.0;      // lanes past the tensor are padding
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) s = s + __shfl_xor(s, o, 64);
+            if (lane == 0) p.partials[j * p.ntiles + t] = s;
+            wave_sync_lds();                                  // W is reused by the next tile
+        }
+        __syncthreads();                                      // every wave is done with this table
     }
 }
 

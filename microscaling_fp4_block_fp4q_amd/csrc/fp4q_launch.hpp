@@ -119,6 +119,7 @@ hipError_t dispatch_quant(const QuantArgs& a, int B, int H, int sf, int st, int 
 template <class InT, int B, int H>
 hipError_t dispatch_gsearch_st(const GSearchArgs& a, int st, int grid, hipStream_t s) {
     if (st == ST_FOUR_OVER_SIX) return launch_resident<k_gsearch<InT, B, H, ST_FOUR_OVER_SIX>>(a, grid, s);
+    if (st == ST_BRUTE_FORCE) return launch_resident<k_gsearch_bf<InT, B, H>>(a, grid, s);
     return launch_resident<k_gsearch<InT, B, H, ST_ABSMAX>>(a, grid, s);
 }
 

@@ -80,7 +80,6 @@ def test_quantize_validation():
     assert quant(F.config(0, 32, 0, F.GLOBAL_SEARCH)) == F.ERR_UNSUPPORTED       # E8M0 + search
     assert quant(F.config(F.UE5M3, 16, 0, F.GLOBAL_TENSOR_AMAX)) == F.ERR_UNSUPPORTED
     assert quant(F.config(F.UE5M3, 16, 0, F.GLOBAL_SEARCH)) == F.ERR_UNSUPPORTED
-    assert quant(F.config(1, 16, F.BRUTE_FORCE, F.GLOBAL_SEARCH)) == F.ERR_UNSUPPORTED
     assert quant(F.config(1, 16, F.GIVEN, F.GLOBAL_SEARCH)) == F.ERR_UNSUPPORTED
     assert quant(F.config(1, 16, 0, F.GLOBAL_SEARCH), g=0) == F.ERR_INVALID_ARG  # writes g
     assert quant(F.config(1, 16, 0, F.GLOBAL_SEARCH), ws=0) == F.ERR_INVALID_ARG # needs workspace

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 E4M3 = F.E4M3
 SEARCH = F.GLOBAL_SEARCH
-NAMES = {F.ABSMAX: "absmax", F.PREVENT_ZERO: "prevent-zero", F.FOUR_OVER_SIX: "4-over-6"}
+NAMES = {F.ABSMAX: "absmax", F.PREVENT_ZERO: "prevent-zero", F.FOUR_OVER_SIX: "4-over-6", F.BRUTE_FORCE: "brute-force"}
 
 
 def small(kind, rows=37, cols=4000):
@@ -39,9 +39,10 @@ def small(kind, rows=37, cols=4000):
 
 @pytest.mark.parametrize("kind", ["normal", "laplace", "normal_1e-4", "outliers"])
 @pytest.mark.parametrize("B", [4, 8, 16, 32])
-@pytest.mark.parametrize("strategy", [F.ABSMAX, F.PREVENT_ZERO, F.FOUR_OVER_SIX])
+@pytest.mark.parametrize("strategy", [F.ABSMAX, F.PREVENT_ZERO, F.FOUR_OVER_SIX, F.BRUTE_FORCE])
 def test_search_small(O_lib, kind, B, strategy):
-    x = small(kind)
+    # brute force inside: 32 exhaustive searches in the oracle, so fewer rows
+    x = small(kind, 5 if strategy == F.BRUTE_FORCE else 37)
     cfg = F.config(E4M3, B, strategy, SEARCH)
     note(f"search {kind} B={B} {NAMES[strategy]} shape={x.shape}")
     gpu = gpu_quantize(x, S.F32, cfg)
@@ -50,11 +51,12 @@ def test_search_small(O_lib, kind, B, strategy):
     compare_quant(gpu, ref)
 
 
+@pytest.mark.parametrize("strategy", [F.ABSMAX, F.BRUTE_FORCE])
 @pytest.mark.parametrize("H", [16, 32])
-def test_search_bf16_rotated(O_lib, H):
-    x = S.cast(S.laplace(40, 2048, 5), S.BF16)
-    cfg = F.config(E4M3, 16, F.ABSMAX, SEARCH, 1.0, H)
-    note(f"search bf16 H={H}")
+def test_search_bf16_rotated(O_lib, H, strategy):
+    x = S.cast(S.laplace(8 if strategy == F.BRUTE_FORCE else 40, 2048, 5), S.BF16)
+    cfg = F.config(E4M3, 16, strategy, SEARCH, 1.0, H)
+    note(f"search bf16 H={H} {NAMES[strategy]}")
     gpu = gpu_quantize(x, S.BF16, cfg, dq_dt=S.BF16)
     ref = oracle_quantize(x, S.BF16, cfg, dq_dt=S.BF16)
     assert gpu["g"].view(np.uint32) == ref["g"].view(np.uint32)
@@ -75,10 +77,11 @@ def test_search_row_stride(O_lib):
         assert_same(S.from_torch(r[k]), ref[k], k)
 
 
-def test_scale_search_entry(O_lib):
+@pytest.mark.parametrize("strategy", [F.FOUR_OVER_SIX, F.BRUTE_FORCE])
+def test_scale_search_entry(O_lib, strategy):
     x = small("laplace", 21, 1024)
-    cfg = F.config(E4M3, 16, F.FOUR_OVER_SIX, SEARCH)
-    note("scale_search entry with SEARCH")
+    cfg = F.config(E4M3, 16, strategy, SEARCH)
+    note(f"scale_search entry with SEARCH {NAMES[strategy]}")
     r = F.scale_search(S.to_torch(x, S.F32, DEV), cfg)
     torch.cuda.synchronize()
     ref = oracle_quantize(x, S.F32, cfg)

@@ -18,7 +18,7 @@ import torch
 import exact_ref as X
 
 E4M3 = 1
-ABSMAX, PZ, FOS = 0, 1, 2
+ABSMAX, PZ, FOS, BF = 0, 1, 2, 3
 TAMAX, SEARCH = 1, 3
 J = 32
 
@@ -125,3 +125,38 @@ def test_search_special_tensors(O):
     assert np.isnan(g)
     r = O.quantize(x, fmt=E4M3, block=16, strategy=ABSMAX, global_mode=SEARCH)
     assert np.all(r["scales"] == 0x7F)
+
+
+def test_brute_force_search_never_above_prevent_zero(O):
+    """With brute force inside, each candidate's total is at most the
+    prevent-zero total at the same candidate: per block the exhaustive
+    minimum runs over codes 1..126, which include prevent-zero's code, and
+    the fp64 tree sum is monotone in its terms."""
+    for kind in ("normal", "laplace", "outlier"):
+        for B in (4, 16):
+            x = tensor(21 + B, 8, 128, kind)
+            gb, tb = O.global_scale_search(x, block=B, strategy=BF)
+            gp, tp = O.global_scale_search(x, block=B, strategy=PZ)
+            assert np.all(tb <= tp), (kind, B, np.argmax(tb - tp))
+            assert gb == np.float32(np.float32(np.abs(x).max() / np.float32(2688.0)) *
+                                    np.float32(1.0 - int(np.argmin(tb)) / 64.0))
+            assert np.all(tb[np.argmin(tb)] < tb[:np.argmin(tb)])   # ties go to the least shrink
+
+
+def test_brute_force_search_matches_exact_totals(O):
+    """Brute force inside the search on 8 blocks of 4: every candidate's
+    total against exact rationals (each block at its exact-minimum code over
+    1..126, S = fl(dec(code) g) as the format defines it)."""
+    x = tensor(7, 1, 32, "laplace")
+    B = 4
+    g, totals = O.global_scale_search(x, block=B, strategy=BF)
+    g0 = np.float32(np.abs(x).max() / np.float32(2688.0))
+    blocks = x.reshape(-1, B)
+    for j in range(J):
+        gj = np.float32(g0 * np.float32(1.0 - j / 64.0))
+        tot = Fraction(0)
+        for blk in blocks:
+            tot += min(X.block_sse_exact(blk, Fraction(float(np.float32(np.float32(float(X.E4M3[c])) * gj))))
+                       for c in range(1, 0x7F))
+        w = float(tot)
+        assert abs(totals[j] - w) <= 1e-6 * w + 1e-30, (j, totals[j], w)
