@@ -434,7 +434,7 @@ __device__ __forceinline__ unsigned long long bf_window(const float (&y)[U], flo
     // every element encodes to zero at the smallest scale: all codes tie
     if (a_b <= t.t0[CLO]) {
         c_lo = c_hi = CLO;
-        return pack_candidate(0.0f, CLO);   // SSE of code CLO is re-computed by the final encode
+        return pack_candidate(0.0f, CLO);   // callers recompute the SSE at the winning code
     }
     float rc[B];
     const float2 e1 = t.sr[c_first], e2 = t.sr[c_second];
@@ -936,13 +936,16 @@ struct BfWaveLds {
 // lane independent candidates to interleave; a window is padded to whole
 // items).  A lane walks its slice, evaluates the items with the block's
 // values read from LDS, and merges its per-block minimum into an LDS 64-bit
-// atomic minimum over (SSE bits, code).  On return W.best[lane * NB + b]
+// atomic minimum over (SSE bits, code).  FAST: every candidate scale is in
+// the division-free range (BfTable::fast; the choice is a template
+// parameter so that no per-candidate branch is left for the compiler to
+// speculate both ways).  On return W.best[lane * NB + b]
 // holds the winning code of each finite block in its low word (its high
 // word is the SSE the search saw, 0 for a block whose elements all encode
 // to zero at every scale), and nan_blk[b] flags blocks with a NaN or
 // infinite value or a non-finite g.  Idle lanes (active false) must hold
 // zeros in y.
-template <int SF, int B, int U>
+template <int SF, int B, int U, bool FAST>
 __device__ __forceinline__ void bf_search_tile(const float (&y)[U], bool active, float g, float inv_six_g,
                                                float inv_four_g, const BfTable& s_bf, BfWaveLds<U, B>& W, int lane,
                                                bool (&nan_blk)[U / B]) {
@@ -953,7 +956,6 @@ __device__ __forceinline__ void bf_search_tile(const float (&y)[U], bool active,
     constexpr int K = B >= 16 ? 1 : 16 / B;       // candidates of one block per work item
     // an item reads codes c0 .. c0 + K - 1 with c0 < CEND
     static_assert(CEND + K - 1 <= 256 + BfTable::kPad, "items read past the table");
-    const bool fast = s_bf.fast;
 
     // publish the fp32 values of this lane's unit
 #pragma unroll
@@ -983,8 +985,7 @@ __device__ __forceinline__ void bf_search_tile(const float (&y)[U], bool active,
                 c2 = s4 > 0u ? s4 : 1u;
             }
             uint32_t lo, hi;
-            if (fast) best = bf_window<SF, B, b * B, true>(y, a_b, c1, c2, s_bf, lo, hi);
-            else best = bf_window<SF, B, b * B, false>(y, a_b, c1, c2, s_bf, lo, hi);
+            best = bf_window<SF, B, b * B, FAST>(y, a_b, c1, c2, s_bf, lo, hi);
             clo[b] = lo;
             n[b] = hi > lo ? (hi - lo + K - 1) / K : 0u;     // work items of K codes
         }
@@ -1052,9 +1053,7 @@ __device__ __forceinline__ void bf_search_tile(const float (&y)[U], bool active,
                 const uint32_t c = c0 + q;
                 const float2 e = es[q];
                 float rc[B];
-                float sse;
-                if (fast) sse = encode_block<SF, B, 0, false, true>(yb, e.x, e.y, rc);
-                else sse = encode_block<SF, B, 0, false, false>(yb, e.x, e.y, rc);
+                const float sse = encode_block<SF, B, 0, false, FAST>(yb, e.x, e.y, rc);
                 const unsigned long long cand = pack_candidate(sse, c);
                 local = cand < local ? cand : local;
             }
@@ -1121,6 +1120,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
     // start gives the same result), so reciprocals replace the divisions
     const float inv_six_g = 1.0f / (6.0f * g), inv_four_g = 1.0f / (4.0f * g);
     fill_bf_table<SF>(s_bf, g);
+    const bool fast = s_bf.fast;
 
     const int64_t ntiles = (p.units + kTileUnits - 1) / kTileUnits;
     const int64_t tstride = (int64_t)gridDim.x * (kThreads / 64);
@@ -1133,7 +1133,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
         float y[U];
         bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
         bool nan_blk[NB];
-        bf_search_tile<SF, B, U>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+        if (fast) bf_search_tile<SF, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+        else bf_search_tile<SF, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
 
         // encode every block at its winning code
         uint32_t cw[code_words(U)];
@@ -1185,6 +1186,7 @@ __global__ __launch_bounds__(kThreads) void k_gsearch_bf(GSearchArgs p) {
         const float g = g0 * search_factor(j);
         const float inv_six_g = 1.0f / (6.0f * g), inv_four_g = 1.0f / (4.0f * g);
         fill_bf_table<SF_E4M3>(s_bf, g);
+        const bool fast = s_bf.fast;
         for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < ntiles; t += tstride) {
             const int64_t u0 = t * kTileUnits;
             const int nvalid = (int)min<int64_t>(kTileUnits, p.units - u0);
@@ -1192,7 +1194,8 @@ __global__ __launch_bounds__(kThreads) void k_gsearch_bf(GSearchArgs p) {
             float y[U];
             bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
             bool nan_blk[NB];
-            bf_search_tile<SF_E4M3, B, U>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            if (fast) bf_search_tile<SF_E4M3, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            else bf_search_tile<SF_E4M3, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
             double e[NB];
             static_for<NB>([&](auto bi) {
                 constexpr int b = decltype(bi)::value;
