@@ -1,6 +1,7 @@
 """Writes search_full_4096.json: the oracle's MSE-searched per-tensor scale
 of the fp32 4096 x 4096 N(0,1) workload tensor (seed 1) at block 16, for
-abs-max and 4-over-6.  Calls only oracle/ and the seeded input generator;
+abs-max, 4-over-6 and brute force (32 exhaustive searches of the tensor:
+about half an hour).  Calls only oracle/ and the seeded input generator;
 the search over the full tensor takes the oracle minutes, too long to redo
 inside a GPU test.  Run: python tests/golden/make_search_golden.py"""
 import json
@@ -21,7 +22,7 @@ def main():
     out = {"what": "oracle search_global_scale on synth.config2()['normal'] (fp32 4096x4096 N(0,1), seed 1), "
                    "E4M3 block 16; g as fp32 bits, j = argmin candidate, totals = fp64 tree sums",
            "cases": {}}
-    for name, st in (("absmax", O.ABSMAX), ("4-over-6", O.FOUR_OVER_SIX)):
+    for name, st in (("absmax", O.ABSMAX), ("4-over-6", O.FOUR_OVER_SIX), ("brute-force", O.BRUTE_FORCE)):
         g, totals = O.global_scale_search(x, block=16, strategy=st)
         out["cases"][name] = {"g_bits": int(np.float32(g).view(np.uint32)), "g": float(g),
                               "j": int(np.argmin(totals)), "totals": [float(t) for t in totals]}

@@ -130,12 +130,13 @@ def test_search_quarter_size_live(O_lib):
     compare_quant(gpu, ref, rows)
 
 
-@pytest.mark.parametrize("strategy", [F.ABSMAX, F.FOUR_OVER_SIX])
+@pytest.mark.parametrize("strategy", [F.ABSMAX, F.FOUR_OVER_SIX, F.BRUTE_FORCE])
 def test_search_full_size_sampled(O_lib, strategy):
     """4096 x 4096 fp32 at B = 16 (two reduction levels past the tiles): the
     oracle's search over the whole tensor is stored in
     tests/golden/search_full_4096.json by make_search_golden.py (it takes the
-    oracle minutes); outputs are compared on sampled rows at that g."""
+    oracle minutes, half an hour with brute force inside); outputs are
+    compared on sampled rows at that g."""
     gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "search_full_4096.json")))
     want = gold["cases"][NAMES[strategy]]
     g = np.uint32(want["g_bits"]).view(np.float32)
