@@ -182,3 +182,23 @@ def test_boundary_blocks_every_strategy(O_lib, strategy):
     ref = oracle_quantize(x, S.F32, cfg)
     assert gpu["g"].view(np.uint32) == ref["g"].view(np.uint32)
     compare_quant(gpu, ref)
+
+
+@pytest.mark.parametrize("g,xs", [(2.0 ** -110, 50.0 * 2.0 ** -110), (2.0 ** -120, 50.0 * 2.0 ** -120),
+                                  (1.0e33, 5.0e34), (2.0 ** -95, 2.0 ** -22)])
+@pytest.mark.parametrize("B", [4, 16])
+def test_brute_force_extreme_global_scale(O_lib, g, xs, B):
+    """User scales that put block scales outside the division-free range
+    (below 2^-100, fp32 subnormals at 2^-120, or above 2^100): brute force
+    takes the IEEE division for every candidate.  In fp32 such scales leave
+    every code with the same SSE: with values near the scales the squared
+    errors underflow to 0 or overflow to inf, and values of 2^-22 against
+    g = 2^-95 saturate at a dequantized value below half an ulp of the
+    value, which the difference absorbs.  The smallest code wins; the test
+    checks that the division path reaches the oracle's ties and outputs."""
+    x = (S.laplace(9, 512, 31) * np.float32(xs)).astype(np.float32)
+    cfg = F.config(E4M3, B, F.BRUTE_FORCE, F.GLOBAL_USER, g)
+    note(f"brute force with g={g} x scale={xs} B={B}")
+    gpu = gpu_quantize(x, S.F32, cfg)
+    ref = oracle_quantize(x, S.F32, cfg)
+    compare_quant(gpu, ref)
