@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 4
+#define FP4Q_ABI_VERSION 5
 
 typedef enum {
     FP4Q_OK = 0,
@@ -240,9 +240,12 @@ fp4q_status fp4q_code_histogram(const uint8_t* codes, int64_t rows, int64_t cols
  * Accumulation is fp32 inside the matrix cores, in an order of its own.
  * workspace: fp4q_mxfp4_gemm_workspace_bytes(M, N, K) bytes of device
  * memory, 256-byte aligned, owned by the caller (the scales rearranged for
- * the matrix cores go there; its contents need no initialisation and are
- * dead after the call).  K must be a positive multiple of 256 and M * K / 2,
- * N * K / 2 below 2^32 (FP4Q_ERR_SHAPE); codes and C 16-byte aligned,
+ * the matrix cores go there, and the padded operand copies described below;
+ * its contents need no initialisation and are dead after the call).  K must be a positive multiple of 32 (one scale
+ * block) and M * Kp / 2, N * Kp / 2 below 2^32, Kp = K rounded up to a
+ * multiple of 256 (FP4Q_ERR_SHAPE).  When K is not a multiple of 256 both
+ * operands are first copied into the workspace with K padded to Kp (zero
+ * codes, which add exactly 0); codes and C 16-byte aligned,
  * ldc * element size a multiple of 16, scales 4-byte aligned, workspace
  * 256-byte aligned (FP4Q_ERR_ALIGNMENT). */
 size_t fp4q_mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -408,7 +408,7 @@ fp4q_status fp4q_code_histogram(const uint8_t* codes, int64_t rows, int64_t cols
 }
 
 size_t fp4q_mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M <= 0 || N <= 0 || K <= 0 || K % 256 != 0) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0) return 0;
     return mxfp4_gemm_workspace(M, N, K);
 }
 
@@ -417,11 +417,11 @@ fp4q_status fp4q_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, con
                             int64_t ldc, void* workspace, void* stream) {
     if (M < 0 || N < 0 || K < 0) return FP4Q_ERR_INVALID_ARG;
     if (c_dt != FP4Q_F32 && c_dt != FP4Q_BF16) return FP4Q_ERR_INVALID_ARG;
-    if (K % 256 != 0) return FP4Q_ERR_SHAPE;
+    if (K % 32 != 0) return FP4Q_ERR_SHAPE;
     if (M == 0 || N == 0) return FP4Q_OK;
     if (K == 0 || ldc < N) return FP4Q_ERR_SHAPE;
-    if ((uint64_t)M * (uint64_t)(K / 2) >= (1ull << 32) || (uint64_t)N * (uint64_t)(K / 2) >= (1ull << 32))
-        return FP4Q_ERR_SHAPE;
+    const uint64_t kp = (uint64_t)(K + 255) / 256 * 256;      // K as the matrix cores run it
+    if ((uint64_t)M * (kp / 2) >= (1ull << 32) || (uint64_t)N * (kp / 2) >= (1ull << 32)) return FP4Q_ERR_SHAPE;
     if (!c || !a_codes || !a_scales || !b_codes || !b_scales || !workspace) return FP4Q_ERR_INVALID_ARG;
     if (!aligned16(c) || (ldc * elem_size(c_dt)) % 16 != 0) return FP4Q_ERR_ALIGNMENT;
     if (!aligned16(a_codes) || !aligned16(b_codes) || ((uintptr_t)a_scales & 3u) || ((uintptr_t)b_scales & 3u) ||

@@ -424,14 +424,53 @@ __global__ __launch_bounds__(256, 1) void k_mxfp4_gemm(GemmArgs p) {
     else gemm_store<uint16_t>(p, acc, buf, r0, c0, lane, full);
 }
 
-size_t mxfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+// Copy of an operand with K padded to Kp (a multiple of the K-step): block
+// j of a row (32 values: 16 code bytes and one scale byte) is copied for
+// j < K / 32, and the padding holds code 0 (+0, which adds exactly 0 to
+// every product whatever its scale) with scale 1.  One lane per block.
+__global__ void k_gemm_pad(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t rows,
+                           int64_t kb, int64_t kbp, uint8_t* __restrict__ pcodes, uint8_t* __restrict__ pscales) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= rows * kbp) return;
+    const int64_t r = i / kbp, j = i - r * kbp;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    uint8_t sc = 127;
+    if (j < kb) {
+        v = *reinterpret_cast<const uint4*>(codes + (r * kb + j) * 16);
+        sc = scales[r * kb + j];
+    }
+    *reinterpret_cast<uint4*>(pcodes + i * 16) = v;
+    pscales[i] = sc;
+}
+
+namespace {
+
+constexpr int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// Bytes of the rearranged scales of both operands for K a multiple of the K-step.
+size_t shuffled_scales_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t steps = K / kGemmStepK;
-    const auto part = [&](int64_t rows) { return (size_t)((((rows + 31) / 32) * steps * 256 + 255) / 256 * 256); };
+    const auto part = [&](int64_t rows) { return (size_t)round256(((rows + 31) / 32) * steps * 256); };
     return part(M) + part(N);
+}
+
+hipError_t launch_mxfp4_gemm_padded_k(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                                      int64_t M, int64_t N, int64_t K, void* c, int c_dt, int64_t ldc, void* workspace,
+                                      hipStream_t s);
+
+}  // namespace
+
+size_t mxfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+    if (K % kGemmStepK == 0) return shuffled_scales_bytes(M, N, K);
+    // K padded to the K-step: both operands copied, then the rearranged scales
+    const int64_t Kp = (K + kGemmStepK - 1) / kGemmStepK * kGemmStepK;
+    return shuffled_scales_bytes(M, N, Kp) + (size_t)(round256(M * Kp / 2) + round256(N * Kp / 2) +
+                                                      round256(M * Kp / 32) + round256(N * Kp / 32));
 }
 
 hipError_t launch_mxfp4_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
                              int64_t N, int64_t K, void* c, int c_dt, int64_t ldc, void* workspace, hipStream_t s) {
+    if (K % kGemmStepK != 0) return launch_mxfp4_gemm_padded_k(a, as, b, bs, M, N, K, c, c_dt, ldc, workspace, s);
     GemmArgs p{};
     p.a = a;
     p.b = b;
@@ -461,5 +500,31 @@ hipError_t launch_mxfp4_gemm(const uint8_t* a, const uint8_t* as, const uint8_t*
     else hipLaunchKernelGGL(k_mxfp4_gemm<0>, grid, block, 0, s, p);
     return hipGetLastError();
 }
+
+namespace {
+
+hipError_t launch_mxfp4_gemm_padded_k(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                                      int64_t M, int64_t N, int64_t K, void* c, int c_dt, int64_t ldc, void* workspace,
+                                      hipStream_t s) {
+    const int64_t Kp = (K + kGemmStepK - 1) / kGemmStepK * kGemmStepK;
+    uint8_t* w = reinterpret_cast<uint8_t*>(workspace) + shuffled_scales_bytes(M, N, Kp);
+    uint8_t* pa = w;
+    uint8_t* pb = pa + round256(M * Kp / 2);
+    uint8_t* pas = pb + round256(N * Kp / 2);
+    uint8_t* pbs = pas + round256(M * Kp / 32);
+    const int64_t kb = K / 32, kbp = Kp / 32;
+    const auto pad = [&](const uint8_t* codes, const uint8_t* scales, int64_t rows, uint8_t* pc, uint8_t* ps) {
+        const int64_t n = rows * kbp;
+        hipLaunchKernelGGL(k_gemm_pad, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, scales, rows, kb,
+                           kbp, pc, ps);
+    };
+    pad(a, as, M, pa, pas);
+    pad(b, bs, N, pb, pbs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_mxfp4_gemm(pa, pas, pb, pbs, M, N, Kp, c, c_dt, ldc, workspace, s);
+}
+
+}  // namespace
 
 }  // namespace fp4q_dev

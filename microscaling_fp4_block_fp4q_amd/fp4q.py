@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "libfp4q.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "fp4q.h")
 
 # FP4Q_ABI_VERSION and the enums (include/fp4q.h)
-ABI_VERSION = 4
+ABI_VERSION = 5
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE = range(6)
 F32, BF16, F16 = 0, 1, 2
 E8M0, E4M3, UE5M3 = 0, 1, 2

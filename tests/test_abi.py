@@ -125,16 +125,20 @@ def test_gemm_validation_and_workspace():
     # per operand: ceil(rows / 32) fragments x K / 256 steps x 64 lanes x 4 bytes, each part 256-byte aligned
     assert W(8192, 8192, 8192) == 2 * (8192 // 32) * 32 * 256
     assert W(33, 1, 256) == 2 * 256 + 256
-    assert W(4, 4, 128) == 0 and W(0, 4, 256) == 0 and W(4, 4, 0) == 0
+    assert W(4, 4, 48) == 0 and W(0, 4, 256) == 0 and W(4, 4, 0) == 0
+    # K not a multiple of 256: rearranged scales for K rounded up to 512, then the padded copies of
+    # codes (rows x 256 bytes) and scales (rows x 16 bytes), every part 256-byte aligned
+    assert W(33, 1, 288) == (1024 + 512) + (8448 + 256) + (768 + 256)
 
     def g(M=4, N=4, K=256, a=A, sa=A, b=A, sb=A, c=A, dt=F.F32, ldc=4, ws=A):
         return L.fp4q_mxfp4_gemm(P(a), P(sa), P(b), P(sb), M, N, K, P(c), dt, ldc, P(ws), None)
     assert g(M=0) == F.OK and g(N=0) == F.OK                                     # empty: nothing to do
     assert g(M=-1) == F.ERR_INVALID_ARG
     assert g(dt=F.F16) == F.ERR_INVALID_ARG
-    assert g(K=128) == F.ERR_SHAPE and g(K=0) == F.ERR_SHAPE
+    assert g(K=48) == F.ERR_SHAPE and g(K=16) == F.ERR_SHAPE and g(K=0) == F.ERR_SHAPE
     assert g(ldc=3) == F.ERR_SHAPE
     assert g(M=1 << 24, K=1 << 9) == F.ERR_SHAPE                                 # M * K / 2 = 2^32 bytes
+    assert g(M=1 << 24, K=480) == F.ERR_SHAPE                                    # K runs padded to 512
     assert g(ws=0) == F.ERR_INVALID_ARG and g(a=0) == F.ERR_INVALID_ARG and g(sb=0) == F.ERR_INVALID_ARG
     assert g(ws=A + 16) == F.ERR_ALIGNMENT
     assert g(a=A + 8) == F.ERR_ALIGNMENT and g(sa=A + 2) == F.ERR_ALIGNMENT

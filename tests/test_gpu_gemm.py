@@ -56,7 +56,10 @@ def check(got, want, bound_abs, K, bf16=False):
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (256, 256, 1024), (512, 768, 512), (96, 200, 256),
                                    (16, 16, 256), (300, 1000, 768), (256, 256, 1280), (128, 512, 1792),
                                    (520, 264, 2048), (640, 1000, 256), (2700, 600, 256), (2304, 2304, 256),
-                                   (1, 1, 256), (1, 300, 512), (257, 1, 768)])
+                                   (1, 1, 256), (1, 300, 512), (257, 1, 768),
+                                   # K not a multiple of 256: operands padded to the K-step in the workspace
+                                   (64, 96, 32), (100, 200, 96), (257, 130, 288), (300, 1000, 800),
+                                   (128, 128, 4128), (1, 1, 32)])
 def test_random_codes(O_lib, M, N, K):
     a, sa, b, sb = operands(M + N + K, M, N, K)
     note(f"gemm random {M}x{N}x{K}")
@@ -144,7 +147,7 @@ def test_empty_and_validation(O_lib):
     ws = F.gemm_workspace(4, 4, 256, DEV)
     p = lambda t: t.data_ptr()
     assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 0, 4, 256, p(c), F.F32, 4, p(ws), None) == F.OK
-    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 128, p(c), F.F32, 4, p(ws), None) == F.ERR_SHAPE
+    assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 48, p(c), F.F32, 4, p(ws), None) == F.ERR_SHAPE
     assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 0, p(c), F.F32, 4, p(ws), None) == F.ERR_SHAPE
     assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 256, p(c), F.F16, 4, p(ws), None) == F.ERR_INVALID_ARG
     assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 256, p(c), F.F32, 4, None, None) == F.ERR_INVALID_ARG
