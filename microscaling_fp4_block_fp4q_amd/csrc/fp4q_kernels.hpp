@@ -754,6 +754,23 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs p) {
 
     const int64_t ntiles = (p.units + kTileUnits - 1) / kTileUnits;
     const int64_t tstride = (int64_t)gridDim.x * (kThreads / 64);
+    // Units of 16 or more values: each lane loads its own unit of the next
+    // tile while this one is quantized (one tile of loads in flight per wave
+    // during the compute; measured 2-21 % faster for B = 16, 32 and the
+    // rotations).  Smaller units load through the LDS slots, coalesced,
+    // without prefetch (prefetching them measured 0-5 % slower).
+    constexpr bool PREFETCH = U >= 16;
+    float ynext[U];                       // unused without PREFETCH
+    auto fetch = [&](int64_t tt) {
+        const int64_t uu = tt * kTileUnits + lane;
+        if (tt < ntiles && uu < p.units) {
+            load_elems<InT, U>(x + unit_offset<U>(uu, p.units_per_row, p.ld_x, p.contiguous), ynext);
+        } else {
+#pragma unroll
+            for (int i = 0; i < U; ++i) ynext[i] = 0.0f;
+        }
+    };
+    if constexpr (PREFETCH) fetch((int64_t)blockIdx.x * (kThreads / 64) + wave);
     for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < ntiles; t += tstride) {
         const int64_t u0 = t * kTileUnits;
         const int nvalid = (int)min<int64_t>(kTileUnits, p.units - u0);
@@ -761,7 +778,11 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs p) {
         const bool active = lane < nvalid;
 
         float y[U];
-        if (p.contiguous) {
+        if constexpr (PREFETCH) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) y[i] = ynext[i];
+            fetch(t + tstride);
+        } else if (p.contiguous) {
             tile_load<InT, U>(x + u0 * U, nvalid, lds, lane, y);
         } else if (active) {
             load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, false), y);
