@@ -1145,6 +1145,23 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
 
     const int64_t ntiles = (p.units + kTileUnits - 1) / kTileUnits;
     const int64_t tstride = (int64_t)gridDim.x * (kThreads / 64);
+    // Units of 32 values run two waves per SIMD, too few to hide a tile
+    // load: each lane loads its own unit of the wave's next tile before
+    // searching the current one (measured 6-7 % faster; no gain for smaller
+    // units, which run more waves).
+    constexpr bool PREFETCH = U >= 32;
+    const InT* x = reinterpret_cast<const InT*>(p.x);
+    float ynext[U];                       // unused without PREFETCH
+    auto fetch = [&](int64_t tt) {
+        const int64_t uu = tt * kTileUnits + lane;
+        if (tt < ntiles && uu < p.units) {
+            load_elems<InT, U>(x + unit_offset<U>(uu, p.units_per_row, p.ld_x, p.contiguous), ynext);
+        } else {
+#pragma unroll
+            for (int i = 0; i < U; ++i) ynext[i] = 0.0f;
+        }
+    };
+    if constexpr (PREFETCH) fetch((int64_t)blockIdx.x * (kThreads / 64) + wave);
     for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < ntiles; t += tstride) {
         const int64_t u0 = t * kTileUnits;
         const int nvalid = (int)min<int64_t>(kTileUnits, p.units - u0);
@@ -1152,7 +1169,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
         const bool active = lane < nvalid;
 
         float y[U];
-        bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
+        if constexpr (PREFETCH) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) y[i] = ynext[i];
+            fetch(t + tstride);
+            if constexpr (H > 0) fwht_segments<H, U>(y);
+            if (!active) {
+#pragma unroll
+                for (int i = 0; i < U; ++i) y[i] = 0.0f;   // idle lanes contribute empty windows
+            }
+        } else {
+            bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
+        }
         bool nan_blk[NB];
         if (fast) bf_search_tile<SF, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
         else bf_search_tile<SF, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
