@@ -85,6 +85,8 @@ MUTANTS = [
     ("search ties to the larger shrink", "if (j == 0 || total < best_total ||", "if (j == 0 || total <= best_total ||", 1),
     ("search candidate step 1/32", "float g = g0 * (float)(1.0 - j / 64.0);", "float g = g0 * (float)(1.0 - j / 32.0);", 1),
     ("search result ignores the winner", "return g0 * (float)(1.0 - best / 64.0);", "return g0;", 1),
+    ("search scores brute force as abs-max", "int code = choose_scale(SF_E4M3, strategy, yb, B, g, 0);",
+     "int code = choose_scale(SF_E4M3, strategy == ST_BRUTE_FORCE ? ST_ABSMAX : strategy, yb, B, g, 0);", 1),
 ]
 
 
