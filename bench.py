@@ -119,6 +119,20 @@ def summarize(dirs, label, command):
                                              "min_us": float(r["MinNs"]) / 1e3,
                                              "total_ms": float(r["TotalDurationNs"]) / 1e6,
                                              "percent": float(r["Percentage"])}
+        # The trace splits each kernel's dispatches by whether the abs-max
+        # pre-pass ran right before it (TENSOR_AMAX calls) or not; the bench's
+        # roofline averages the launches without it.
+        for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            trace = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
+            split, prev = {}, ""
+            for r in trace:
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                key = "after_amax" if "k_amax" in prev else "without_amax"
+                split.setdefault(r["Kernel_Name"], {"without_amax": [], "after_amax": []})[key].append(us)
+                prev = r["Kernel_Name"]
+            for k, v in split.items():
+                out.setdefault("split", {})[k] = {
+                    key: {"dispatches": len(ds), "avg_us": sum(ds) / len(ds)} for key, ds in v.items() if ds}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             acc = {}
             for r in csv.DictReader(open(f)):
@@ -136,6 +150,18 @@ def summarize(dirs, label, command):
         for k, v in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["total_ms"])[:25]:
             lines.append(f"| `{k[:90]}` | {v['calls']} | {v['avg_us']:.2f} | {v['min_us']:.2f} | "
                          f"{v['total_ms']:.3f} | {v['percent']:.2f} |")
+        lines.append("")
+    if out.get("split") and out["kernels"]:
+        lines += ["Dispatches split by whether the abs-max pre-pass ran right before them (from the kernel trace):", "",
+                  "| kernel | without pre-pass: dispatches | avg us | after pre-pass: dispatches | avg us |",
+                  "|---|---|---|---|---|"]
+        top = [k for k, _ in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["total_ms"])[:25]]
+        for k in top:
+            v = out["split"].get(k, {})
+            a, b = v.get("without_amax"), v.get("after_amax")
+            if not a or not b:
+                continue
+            lines.append(f"| `{k[:90]}` | {a['dispatches']} | {a['avg_us']:.2f} | {b['dispatches']} | {b['avg_us']:.2f} |")
         lines.append("")
     if out["counters"]:
         lines += ["| kernel | counter | mean per dispatch | dispatches |", "|---|---|---|---|"]
