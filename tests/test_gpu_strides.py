@@ -1,0 +1,150 @@
+"""GPU parity with row strides (ld > cols) on every entry point that takes
+one: the input is the left part of a wider host array whose extra columns
+hold NaN, so a kernel that read past cols would change the block maxima and
+every output of those rows; outputs with their own ld are written into wider
+buffers prefilled with a sentinel that must survive.  Expected values come
+from the oracle on the contiguous columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+from microscaling_fp4_block_fp4q_amd import fp4q as F
+from microscaling_fp4_block_fp4q_amd import synth as S
+from oracle import oracle as O
+
+from gpu_helpers import DEV, TORCH_DT, assert_same, note
+
+pytestmark = pytest.mark.gpu
+
+E8M0, E4M3 = F.E8M0, F.E4M3
+ABSMAX, PZ, FOS, BF = F.ABSMAX, F.PREVENT_ZERO, F.FOUR_OVER_SIX, F.BRUTE_FORCE
+NONE, TAMAX, USER = F.GLOBAL_NONE, F.GLOBAL_TENSOR_AMAX, F.GLOBAL_USER
+NAN_BITS = {S.F32: None, S.BF16: 0x7FC0, S.F16: 0x7E00}
+SENTINEL = 7.0                      # exactly representable in all three output types
+
+
+def wide(x: np.ndarray, dt: int, pad: int) -> np.ndarray:
+    """x with `pad` NaN columns appended (fp32, or 16-bit patterns)."""
+    rows = x.shape[0]
+    if dt == S.F32:
+        tail = np.full((rows, pad), np.nan, np.float32)
+    else:
+        tail = np.full((rows, pad), NAN_BITS[dt], np.uint16)
+    return np.ascontiguousarray(np.concatenate([x, tail], axis=1))
+
+
+def strided_input(x, dt, pad):
+    """A [rows, cols] view with ld = cols + pad of a device copy of wide(x)."""
+    return S.to_torch(wide(x, dt, pad), dt, DEV)[:, :x.shape[1]]
+
+
+def strided_output(rows, cols, pad, dt):
+    full = torch.full((rows, cols + pad), SENTINEL, dtype=TORCH_DT[dt], device=DEV)
+    return full, full[:, :cols]
+
+
+def untouched(full, cols):
+    return bool(torch.all(full[:, cols:] == SENTINEL))
+
+
+CASES = [
+    # (fmt, B, strategy, global mode, hadamard, x dtype, x pad, dequant dtype, dequant pad)
+    (E4M3, 4, BF, NONE, 0, S.F32, 12, S.F32, 4),
+    (E4M3, 16, BF, TAMAX, 16, S.BF16, 24, S.BF16, 8),
+    (E8M0, 32, BF, NONE, 0, S.BF16, 8, S.F32, 36),
+    (E4M3, 8, BF, USER, 0, S.F16, 40, S.F16, 16),
+    (E4M3, 4, PZ, TAMAX, 0, S.F32, 4, S.BF16, 24),
+    (E8M0, 32, ABSMAX, NONE, 32, S.BF16, 16, S.BF16, 8),
+    (E4M3, 16, FOS, TAMAX, 0, S.F16, 8, S.F32, 4),
+]
+
+
+FMT = {E8M0: "e8m0", E4M3: "e4m3"}
+ST = {ABSMAX: "absmax", PZ: "pz", FOS: "4over6", BF: "bf"}
+GM = {NONE: "none", TAMAX: "amax", USER: "user"}
+DT = {S.F32: "f32", S.BF16: "bf16", S.F16: "f16"}
+
+
+def case_id(c):
+    fmt, B, st, gm, H, x_dt, _, dq_dt, _ = c
+    return f"{FMT[fmt]}-B{B}-{ST[st]}-{GM[gm]}-H{H}-{DT[x_dt]}-to-{DT[dq_dt]}"
+
+
+@pytest.mark.parametrize("fmt,B,strategy,gm,H,x_dt,x_pad,dq_dt,dq_pad", CASES, ids=[case_id(c) for c in CASES])
+def test_quantize_row_stride(O_lib, fmt, B, strategy, gm, H, x_dt, x_pad, dq_dt, dq_pad):
+    rows, cols = 37, 768
+    x = S.laplace(rows, cols, 41, x_dt)
+    cfg = F.config(fmt, B, strategy, gm, 0.003 if gm == USER else 1.0, hadamard=H)
+    note(f"quantize row stride fmt={fmt} B={B} st={strategy} gm={gm} H={H} x_dt={x_dt} "
+         f"ld_x={cols + x_pad} ld_dq={cols + dq_pad}")
+    xt = strided_input(x, x_dt, x_pad)
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((rows, cols // B), dtype=torch.uint8, device=DEV)
+    g = torch.empty(1, dtype=torch.float32, device=DEV)
+    dq_full, dq = strided_output(rows, cols, dq_pad, dq_dt)
+    mse = torch.empty((rows, cols // B), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(F.workspace_bytes(cfg, rows, cols), 16), dtype=torch.uint8, device=DEV)
+    F.fp4q_quantize(cfg, xt, codes, scales, g, dq, mse, ws)
+    torch.cuda.synchronize()
+    ref = O.quantize(x, x_dt=x_dt, fmt=fmt, block=B, strategy=strategy, global_mode=gm,
+                     user_g=cfg.global_scale, hadamard=H, dq_dt=dq_dt)
+    if gm != NONE:
+        assert S.from_torch(g)[0].view(np.uint32) == np.float32(ref["g"]).view(np.uint32)
+    assert_same(S.from_torch(codes), ref["codes"], "codes")
+    assert_same(S.from_torch(scales), ref["scales"], "scales")
+    assert_same(S.from_torch(dq), ref["dequant"], "dequant")
+    assert_same(S.from_torch(mse), ref["mse"], "mse")
+    assert untouched(dq_full, cols), "dequant written past cols"
+
+
+@pytest.mark.parametrize("fmt,B,gm,H,x_dt,out_dt", [(E4M3, 16, TAMAX, 0, S.F32, S.BF16),
+                                                    (E8M0, 32, NONE, 32, S.BF16, S.F32),
+                                                    (E4M3, 4, NONE, 16, S.F16, S.F16)])
+def test_dequantize_and_block_mse_row_stride(O_lib, fmt, B, gm, H, x_dt, out_dt):
+    rows, cols = 29, 1024
+    x = S.normal(rows, cols, 43, x_dt)
+    ref = O.quantize(x, x_dt=x_dt, fmt=fmt, block=B, strategy=ABSMAX, global_mode=gm, hadamard=H,
+                     dq_dt=out_dt)
+    cfg = F.config(fmt, B, ABSMAX, gm, hadamard=H)
+    note(f"dequantize/block_mse row stride fmt={fmt} B={B} H={H} x_dt={x_dt} out={out_dt}")
+    codes = torch.from_numpy(ref["codes"]).to(DEV)
+    scales = torch.from_numpy(ref["scales"]).to(DEV)
+    g = None if gm == NONE else torch.tensor([ref["g"]], dtype=torch.float32, device=DEV)
+    out_full, out = strided_output(rows, cols, 8 if out_dt == S.F32 else 16, out_dt)
+    F.fp4q_dequantize(cfg, codes, scales, out, g)
+    mse = torch.empty((rows, cols // B), dtype=torch.float32, device=DEV)
+    F.fp4q_block_mse(cfg, strided_input(x, x_dt, 32), codes, scales, mse, g)
+    torch.cuda.synchronize()
+    assert_same(S.from_torch(out), ref["dequant"], "dequant")
+    assert untouched(out_full, cols), "dequant written past cols"
+    assert_same(S.from_torch(mse), ref["mse"], "mse")
+
+
+@pytest.mark.parametrize("fmt", [E8M0, E4M3])
+def test_focus_row_stride(O_lib, fmt):
+    rows, cols, K = 33, 512, 8
+    w, c, grad = S.focus_inputs(rows, cols, K, seeds=(44, 45, 46))
+    cfg = F.mxfp4() if fmt == E8M0 else F.nvfp4()
+    q = O.quantize(w, x_dt=S.BF16, fmt=cfg.scale_fmt, block=cfg.block, strategy=ABSMAX,
+                   global_mode=cfg.global_mode, dq_dt=None)
+    note(f"focus row stride fmt={fmt} ld_w={cols + 24} ld_out={cols + 8} ld_g={cols + 40}")
+    wt = strided_input(w, S.BF16, 24)
+    gt = strided_input(grad, S.BF16, 40)
+    st = torch.from_numpy(q["scales"]).to(DEV)
+    ct = S.to_torch(c, S.F16, DEV)
+    gd = None if fmt == E8M0 else torch.tensor([q["g"]], dtype=torch.float32, device=DEV)
+    wh_full, wh = strided_output(rows, cols, 8, S.BF16)
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    grad_c = torch.empty((rows, cols // K), dtype=torch.float32, device=DEV)
+    F.fp4q_relaxed_fakequant_fwd(cfg, wt, st, ct, K, wh, gd, codes)
+    F.fp4q_relaxed_fakequant_bwd(cfg, wt, st, ct, K, gt, grad_c, gd)
+    torch.cuda.synchronize()
+    rw, rc = O.relaxed_fwd(w, q["scales"], q["g"], c, fmt=cfg.scale_fmt, block=cfg.block, sub_block=K,
+                           w_dt=S.BF16)
+    rg = O.relaxed_bwd(w, q["scales"], q["g"], c, grad, fmt=cfg.scale_fmt, block=cfg.block, sub_block=K,
+                       w_dt=S.BF16, g_dt=S.BF16)
+    assert_same(S.from_torch(wh), rw, "w_hat")
+    assert untouched(wh_full, cols), "w_hat written past cols"
+    assert_same(S.from_torch(codes), rc, "codes")
+    assert_same(S.from_torch(grad_c), rg, "grad_c")
