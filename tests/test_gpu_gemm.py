@@ -154,3 +154,29 @@ def test_empty_and_validation(O_lib):
     assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 256, p(c), F.F32, 4, p(ws) + 16, None) == \
         F.ERR_ALIGNMENT
     assert L.fp4q_mxfp4_gemm(p(z), p(z), p(z), p(z), 4, 4, 256, p(c), F.F32, 3, p(ws), None) == F.ERR_SHAPE
+
+
+def test_operand_at_the_size_limit(O_lib):
+    """A's codes one row short of 2^32 bytes (M = 2^20 - 1 at K = 8192; one
+    more row is refused): the direct loads' 32-bit buffer offsets reach their
+    top and the last tile of rows is ragged.  A's codes are 256 copies of a
+    seeded 4096-row block, built on the device; its scales are drawn for
+    every row.  Sampled rows of C are compared with the oracle."""
+    M, N, K = (1 << 20) - 1, 256, 8192
+    assert M * (K // 2) < 2 ** 32 <= (M + 1) * (K // 2)
+    rng = np.random.default_rng(81)
+    base = rng.integers(0, 256, (4096, K // 2), dtype=np.uint8)
+    sa = rng.integers(127 - 4, 127 + 5, (M, K // 32), dtype=np.uint8)
+    _, _, b, sb = operands(82, 1, N, K)
+    note(f"gemm at the operand size limit {M}x{N}x{K}")
+    a_dev = torch.from_numpy(base).to(DEV).repeat(256, 1)[:M]
+    t = [a_dev] + [torch.from_numpy(v).to(DEV) for v in (sa, b, sb)]
+    c = F.mxfp4_gemm(*t, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = [0, 1, 4095, 4096, 1 << 19, M - 256, M - 255, M - 2, M - 1]
+    got = c[rows].cpu().numpy().astype(np.float64)
+    del a_dev, t, c
+    torch.cuda.empty_cache()
+    a_rows = base[[r % 4096 for r in rows]]
+    want = O.mxfp4_gemm(a_rows, sa[rows], b, sb)
+    check(got, want, abs_product(a_rows, sa[rows], b, sb), K)
