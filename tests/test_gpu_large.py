@@ -36,15 +36,20 @@ def host_rows(base_bits, rows):
     return S.cast(f * np.array([copy_factor(r) for r in rows])[:, None], S.BF16)
 
 
-def test_tensor_past_2_31_elements(O_lib):
-    assert ROWS * COLS > 2 ** 31 and SAMPLE[5] * COLS == 2 ** 31
-    base = S.normal(BASE_ROWS, COLS, 71, S.BF16)
-    note(f"large tensor bf16 [{ROWS}, {COLS}]: build on the device")
+def build_large(base):
+    """The [ROWS, COLS] device tensor whose copy k is base * copy_factor."""
     base_dev = S.to_torch(base, S.BF16, DEV)
     x = torch.empty((ROWS, COLS), dtype=torch.bfloat16, device=DEV)
     for k in range(COPIES):
         torch.mul(base_dev, copy_factor(k * BASE_ROWS), out=x[k * BASE_ROWS:(k + 1) * BASE_ROWS])
-    del base_dev
+    return x
+
+
+def test_tensor_past_2_31_elements(O_lib):
+    assert ROWS * COLS > 2 ** 31 and SAMPLE[5] * COLS == 2 ** 31
+    base = S.normal(BASE_ROWS, COLS, 71, S.BF16)
+    note(f"large tensor bf16 [{ROWS}, {COLS}]: build on the device")
+    x = build_large(base)
 
     nv = F.nvfp4(F.FOUR_OVER_SIX)
     bf = F.config(F.E4M3, 16, F.BRUTE_FORCE, F.GLOBAL_NONE)
@@ -92,3 +97,41 @@ def test_tensor_past_2_31_elements(O_lib):
     assert_same(got["s2"], r2["scales"], "brute-force scales")
     del c1, s1, dq1, m1, c2, s2, ws
     torch.cuda.empty_cache()
+
+
+def test_focus_past_2_31_elements(O_lib):
+    """FOCUS forward and backward (MXFP4, sub-blocks of 8) on the same kind
+    of tensor, used both as W and as the upstream gradient G.  The block
+    scales are seeded E8M0 codes drawn on the host for every block (the
+    relaxed quantizer takes them as an input); c repeats a seeded block."""
+    K = 8
+    cfg = F.mxfp4()
+    base = S.normal(BASE_ROWS, COLS, 72, S.BF16, sigma=0.02)
+    rng = np.random.default_rng(73)
+    scales = rng.integers(118, 124, (ROWS, COLS // 32), dtype=np.uint8)
+    _, c_base, _ = S.focus_inputs(BASE_ROWS, 64, K, seeds=(74, 75, 76))     # c_base [4096, 8] fp16 bits
+    c_base = np.tile(c_base, (1, COLS // 64))                                 # [4096, COLS / 8]
+    note(f"large FOCUS bf16 [{ROWS}, {COLS}] K={K}: build on the device")
+    w = build_large(base)
+    c = S.to_torch(c_base, S.F16, DEV).repeat(COPIES, 1)
+    st = torch.from_numpy(scales).to(DEV)
+    w_hat = torch.empty_like(w)
+    codes = torch.empty((ROWS, COLS // 2), dtype=torch.uint8, device=DEV)
+    grad_c = torch.empty((ROWS, COLS // K), dtype=torch.float32, device=DEV)
+    note("large FOCUS: forward")
+    F.fp4q_relaxed_fakequant_fwd(cfg, w, st, c, K, w_hat, None, codes)
+    torch.cuda.synchronize()
+    note("large FOCUS: backward")
+    F.fp4q_relaxed_fakequant_bwd(cfg, w, st, c, K, w, grad_c, None)
+    torch.cuda.synchronize()
+    got = {n: S.from_torch(t[SAMPLE]) for n, t in (("w_hat", w_hat), ("codes", codes), ("grad_c", grad_c))}
+    del w, c, st, w_hat, codes, grad_c
+    torch.cuda.empty_cache()
+    wr = host_rows(base, SAMPLE)
+    cr = c_base[[r % BASE_ROWS for r in SAMPLE]]
+    rw, rc = O.relaxed_fwd(wr, scales[SAMPLE], 1.0, cr, fmt=F.E8M0, block=32, sub_block=K, w_dt=S.BF16)
+    rg = O.relaxed_bwd(wr, scales[SAMPLE], 1.0, cr, wr, fmt=F.E8M0, block=32, sub_block=K, w_dt=S.BF16,
+                       g_dt=S.BF16)
+    assert_same(got["w_hat"], rw, "w_hat")
+    assert_same(got["codes"], rc, "codes")
+    assert_same(got["grad_c"], rg, "grad_c")
