@@ -17,7 +17,7 @@ from gpu_helpers import DEV, TORCH_DT, assert_same, note
 
 pytestmark = pytest.mark.gpu
 
-E8M0, E4M3 = F.E8M0, F.E4M3
+E8M0, E4M3, UE5M3 = F.E8M0, F.E4M3, F.UE5M3
 ABSMAX, PZ, FOS, BF = F.ABSMAX, F.PREVENT_ZERO, F.FOUR_OVER_SIX, F.BRUTE_FORCE
 NONE, TAMAX, USER = F.GLOBAL_NONE, F.GLOBAL_TENSOR_AMAX, F.GLOBAL_USER
 NAN_BITS = {S.F32: None, S.BF16: 0x7FC0, S.F16: 0x7E00}
@@ -57,10 +57,12 @@ CASES = [
     (E4M3, 4, PZ, TAMAX, 0, S.F32, 4, S.BF16, 24),
     (E8M0, 32, ABSMAX, NONE, 32, S.BF16, 16, S.BF16, 8),
     (E4M3, 16, FOS, TAMAX, 0, S.F16, 8, S.F32, 4),
+    (UE5M3, 16, BF, NONE, 0, S.F32, 8, S.F32, 12),
+    (UE5M3, 4, FOS, USER, 16, S.BF16, 8, S.BF16, 16),
 ]
 
 
-FMT = {E8M0: "e8m0", E4M3: "e4m3"}
+FMT = {E8M0: "e8m0", E4M3: "e4m3", UE5M3: "ue5m3"}
 ST = {ABSMAX: "absmax", PZ: "pz", FOS: "4over6", BF: "bf"}
 GM = {NONE: "none", TAMAX: "amax", USER: "user"}
 DT = {S.F32: "f32", S.BF16: "bf16", S.F16: "f16"}
