@@ -22,14 +22,23 @@ All inputs are generated once and are resident in HBM before timing; every
 output buffer is preallocated; the timed region holds only library calls.
 value = algorithmic bytes of the step (each input read once, each output
 written once) / step time.  Per-call HIP events over the timed steps give
-the per-strategy rates and the roofline of the dominant kernel.
+the per-strategy rates and the roofline of the dominant kernel.  A cold
+leg times every call once more with the caches flushed before it (1 GiB of
+reads and writes on the same stream, outside the events).
+
+Beside the step, the other workloads are timed per call, warm and cold:
+fp32 1024 x 1024 (launch-bound, reported only), the Llama-3.1-8B-shaped
+bf16 MLP weights, bf16 8192 x 4096 activations with the fused rotation, and
+the bf16 4096 x 12288 FOCUS fake-quant.
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import ctypes
 import json
 import os
+import platform
 import sys
 import time
 
@@ -40,16 +49,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, published
-VALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12   # 256 CUs x 128 fp32 lanes/clock x 2.4 GHz = 157.3 TFLOP/s / 2
+# fp32 vector peak: 256 CUs x 128 fp32 lanes/clock x 2.4 GHz = 78.6 T lane-instructions/s
+# (the published 157.3 TFLOP/s counts an FMA as two flops)
+VALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12
 BF_INSTR_PER_EVAL = 13.25                   # VALU instructions of one candidate-element evaluation (B=16 loop)
 BF_CANDIDATES = 126                         # positive finite E4M3 scales an exhaustive search evaluates
 CSRC = os.path.join(ROOT, "microscaling_fp4_block_fp4q_amd", "csrc")
+PROBE_LIB = os.path.join(ROOT, "microscaling_fp4_block_fp4q_amd", "libfp4q_probe.so")
 PROFILES = os.path.join(ROOT, "profiles")
+FLUSH_MIB = 1024                            # the cold leg reads 1 GiB before each call
 
 STRATS = {0: "absmax", 1: "prevent-zero", 2: "4-over-6", 3: "brute-force"}
+VALU_PROBES = {0: "v_add_f32", 1: "v_mul_f32", 2: "v_fma_f32", 3: "integer add/xor/shift",
+               4: "fp32 min/max/add", 5: "brute-force candidate evaluation (block of 16)"}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
@@ -57,6 +72,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measurements outside the step (scale search, UE5M3, histogram, GEMM)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config lines of the other workloads (C1, C3, C4, C5)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="rows per tensor in the oracle sample")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--calls-out", default=None, help="write every call's mean time (ms) and bytes to this file")
@@ -64,24 +81,32 @@ def parse():
                     help="summarise rocprofv3 csv output directories into --label under profiles/ and exit")
     ap.add_argument("--label", default=None)
     ap.add_argument("--command", default="", help="the command that produced the --summarize directories")
+    ap.add_argument("--probe-json", default=None,
+                    help="with --summarize: the --probe result line whose VALU probe times the counters divide")
     ap.add_argument("--only", default=None,
                     help="profiling mode: run only the calls whose name contains one of these "
                          "'|'-separated texts, --steps times, and print no result line")
+    ap.add_argument("--configs-only", default=None,
+                    help="profiling mode: run only the per-config calls whose name contains one of these "
+                         "'|'-separated texts, --steps times, and print no result line")
     ap.add_argument("--profile-gemm", action="store_true",
                     help="profiling mode: run only the 8192^3 MXFP4 GEMM, --steps times, and print no result line")
+    ap.add_argument("--probe", action="store_true",
+                    help="run the HBM stream and VALU rate probes, print their JSON line and exit")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="profiling mode: also run a device-to-device copy of this many MiB "
                          "(calibrates the HBM byte counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 class Call:
-    """One preallocated library call of the step."""
+    """One preallocated library call."""
 
     def __init__(self, name, fn, args, nbytes, elems, kind, meta):
         self.name, self.fn, self.args = name, fn, args
         self.nbytes, self.elems, self.kind, self.meta = nbytes, elems, kind, meta
         self.times = []
+        self.cold = []
 
     def __call__(self):
         st = self.fn(*self.args)
@@ -105,9 +130,12 @@ def source_digest(gemm: bool = False) -> str:
     return h.hexdigest()[:16]
 
 
-def summarize(dirs, label, command):
+def summarize(dirs, label, command, probe_json=None):
     """Aggregate rocprofv3 csv output (kernel stats and counter collections)
-    into profiles/<label>.json (numbers) and profiles/<label>.md (table)."""
+    into profiles/<label>.json (numbers) and profiles/<label>.md (table).
+    With probe_json (the line bench.py --probe printed in the same command),
+    the VALU probes' executed lane-instruction rates are derived: SQ_INSTS_VALU
+    x 64 per dispatch over the probe's mean launch time."""
     import csv
     import glob
     gemm = "gemm" in label
@@ -120,8 +148,7 @@ def summarize(dirs, label, command):
                                              "total_ms": float(r["TotalDurationNs"]) / 1e6,
                                              "percent": float(r["Percentage"])}
         # The trace splits each kernel's dispatches by whether the abs-max
-        # pre-pass ran right before it (TENSOR_AMAX calls) or not; the bench's
-        # roofline averages the launches without it.
+        # pre-pass ran right before it (TENSOR_AMAX calls) or not.
         for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
             trace = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
             split, prev = {}, ""
@@ -134,20 +161,48 @@ def summarize(dirs, label, command):
                 out.setdefault("split", {})[k] = {
                     key: {"dispatches": len(ds), "avg_us": sum(ds) / len(ds)} for key, ds in v.items() if ds}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows = list(csv.DictReader(open(f)))
+            key_of = (lambda r: int(r["Dispatch_Id"])) if rows and "Dispatch_Id" in rows[0] else None
+            if key_of:
+                rows.sort(key=key_of)
             acc = {}
-            for r in csv.DictReader(open(f)):
+            for r in rows:
                 acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             for k, cs in acc.items():
                 dst = out["counters"].setdefault(k, {})
                 for c, v in cs.items():
-                    dst[c] = {"mean": sum(v) / len(v), "dispatches": len(v)}
+                    dst[c] = {"mean": sum(v) / len(v), "dispatches": len(v), "values": v}
+    rate_lines = []
+    if probe_json:
+        probe = json.loads(open(probe_json).read().strip().splitlines()[-1])
+        out["probe"] = probe
+        out["rates"] = {}
+        rate_lines = ["VALU probes: executed lane-instructions (SQ_INSTS_VALU x 64) over the mean launch time "
+                      "(HIP events, same command):", "",
+                      "| probe | lanes | ms | SQ_INSTS_VALU per dispatch | T lane-instr/s | of 78.6 T |",
+                      "|---|---|---|---|---|---|"]
+        for name, v in probe["valu"].items():
+            kc = next((c for k, c in out["counters"].items() if f"k_valu<{v['kind']}>" in k), None)
+            if not kc or "SQ_INSTS_VALU" not in kc:
+                continue
+            ins = kc["SQ_INSTS_VALU"]["mean"]
+            rate = ins * 64 / (v["ms"] * 1e-3) / 1e12
+            out["rates"][name] = round(rate, 2)
+            rate_lines.append(f"| {name} | {v['lanes']} | {v['ms']:.4f} | {ins:.0f} | {rate:.2f} | "
+                              f"{rate / VALU_PEAK_TOPS:.3f} |")
+        rate_lines += ["", "HBM stream probes (same command):", "", "| stream | GB/s | of 8 TB/s | workgroups |",
+                       "|---|---|---|---|"]
+        for name, v in probe["hbm"].items():
+            rate_lines.append(f"| {name} | {v['GB/s']} | {v['hbm_frac']} | {v['workgroups']} |")
+        rate_lines.append("")
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, label + ".json"), "w") as f:
         json.dump(out, f, indent=1)
     lines = [f"# {label}", "", f"Command: `{command}`", "", f"Kernel sources digest: `{out['source_digest']}`", ""]
+    lines += rate_lines
     if out["kernels"]:
         lines += ["| kernel | calls | avg us | min us | total ms | % |", "|---|---|---|---|---|---|"]
-        for k, v in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["total_ms"])[:25]:
+        for k, v in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["total_ms"])[:30]:
             lines.append(f"| `{k[:90]}` | {v['calls']} | {v['avg_us']:.2f} | {v['min_us']:.2f} | "
                          f"{v['total_ms']:.3f} | {v['percent']:.2f} |")
         lines.append("")
@@ -155,7 +210,7 @@ def summarize(dirs, label, command):
         lines += ["Dispatches split by whether the abs-max pre-pass ran right before them (from the kernel trace):", "",
                   "| kernel | without pre-pass: dispatches | avg us | after pre-pass: dispatches | avg us |",
                   "|---|---|---|---|---|"]
-        top = [k for k, _ in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["total_ms"])[:25]]
+        top = [k for k, _ in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["total_ms"])[:30]]
         for k in top:
             v = out["split"].get(k, {})
             a, b = v.get("without_amax"), v.get("after_amax")
@@ -173,37 +228,39 @@ def summarize(dirs, label, command):
     print(f"wrote profiles/{label}.json and .md")
 
 
-def dominant_profile(kernel_name: str):
-    """Counters of kernel_name from the committed profile, or None when the
-    profile is missing or was taken on other kernel sources."""
-    path = os.path.join(PROFILES, "counters_bench_dominant.json")
+def load_profile(label: str, gemm: bool = False):
+    """A committed profile summary, or None when it is missing or was taken
+    on other kernel sources."""
+    path = os.path.join(PROFILES, label + ".json")
     if not os.path.exists(path):
         return None
     prof = json.load(open(path))
-    if prof.get("source_digest") != source_digest():
+    if prof.get("source_digest") != source_digest(gemm):
+        return None
+    return prof
+
+
+def kernel_counters(prof, kernel_name: str):
+    if not prof:
         return None
     return next((v for k, v in prof["counters"].items() if kernel_name in k), None)
 
 
-def counter_traffic(kernel_name: str):
-    """HBM bytes per launch of kernel_name from the committed counter profile,
-    scaled by a plain copy of known size; None if the profile is missing or
-    was taken on other kernel sources."""
-    path = os.path.join(PROFILES, "counters_bench_dominant.json")
-    if not os.path.exists(path):
-        return None
-    prof = json.load(open(path))
-    if prof.get("source_digest") != source_digest():
-        return None
-    cnt = prof["counters"]
-    copy = next((v for k, v in cnt.items() if "copyBuffer" in k), None)
-    kern = next((v for k, v in cnt.items() if kernel_name in k), None)
+def copy_scaled_traffic(prof, kern):
+    """HBM bytes per dispatch (list) of a kernel's FETCH_SIZE / WRITE_SIZE
+    counters, scaled by what the same counters read for a plain device copy
+    of known size in the same runs; None without both."""
+    cnt = prof["counters"] if prof else {}
+    copy = next((v for k, v in cnt.items() if "copyBuffer" in k or "k_copy" in k), None)
     if not copy or not kern or "FETCH_SIZE" not in kern or "WRITE_SIZE" not in kern:
         return None
     copy_kib = prof.get("copy_mib", 256) * 1024.0
     f_scale = copy_kib / copy["FETCH_SIZE"]["mean"]
     w_scale = copy_kib / copy["WRITE_SIZE"]["mean"]
-    return 1024.0 * (kern["FETCH_SIZE"]["mean"] * f_scale + kern["WRITE_SIZE"]["mean"] * w_scale)
+    fs, ws = kern["FETCH_SIZE"].get("values"), kern["WRITE_SIZE"].get("values")
+    if not fs or not ws or len(fs) != len(ws):
+        fs, ws = [kern["FETCH_SIZE"]["mean"]], [kern["WRITE_SIZE"]["mean"]]
+    return [1024.0 * (f * f_scale + w * w_scale) for f, w in zip(fs, ws)]
 
 
 def gemm_profile():
@@ -211,11 +268,8 @@ def gemm_profile():
     they were taken on the current GEMM source."""
     out = {}
     for label in ("kernel_stats_mxfp4_gemm_8192", "counters_mxfp4_gemm_8192"):
-        path = os.path.join(PROFILES, label + ".json")
-        if not os.path.exists(path):
-            continue
-        prof = json.load(open(path))
-        if prof.get("source_digest") != source_digest(gemm=True):
+        prof = load_profile(label, gemm=True)
+        if not prof:
             continue
         for k, v in prof.get("kernels", {}).items():
             if "k_mxfp4_gemm" in k:
@@ -237,71 +291,224 @@ def quant_bytes(rows, cols, B, in_es=4, dq_es=4, mse=True, dq=True):
     return n * in_es + n // 2 + n // B + (n * dq_es if dq else 0) + (4 * n // B if mse else 0)
 
 
+# --------------------------------------------------------------------------
+# probes: HBM streams and VALU issue rates (libfp4q_probe.so)
+# --------------------------------------------------------------------------
+
+_probe = None
+
+
+def probe_lib():
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is missing: build it with `python -m microscaling_fp4_block_fp4q_amd.build`")
+        L = ctypes.CDLL(PROBE_LIB)
+        L.fp4q_probe_stream.restype = ctypes.c_int
+        L.fp4q_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int, ctypes.c_void_p]
+        L.fp4q_probe_valu.restype = ctypes.c_int
+        L.fp4q_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        _probe = L
+    return _probe
+
+
+def cu_count(torch):
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+class Flusher:
+    """Evicts L2 and the last-level cache without leaving dirty lines behind:
+    a read of 1 GiB (8 loads in flight per lane) on the library's stream."""
+
+    def __init__(self, torch, dev):
+        self.src = torch.ones(FLUSH_MIB << 18, dtype=torch.float32, device=dev)
+        self.grid = 8 * cu_count(torch)
+        self.dst = torch.empty(self.grid * 256, dtype=torch.int32, device=dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def __call__(self):
+        st = probe_lib().fp4q_probe_stream(4, ctypes.c_void_p(self.src.data_ptr()), ctypes.c_void_p(self.dst.data_ptr()),
+                                           self.src.numel() // 4, self.grid, self.stream)
+        if st != 0:
+            raise RuntimeError("cache flush read failed")
+
+
+def events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_fn(torch, fn, reps, flush=None):
+    """Mean ms of fn over reps calls, each bracketed by HIP events on the
+    current stream (after one untimed call); with flush, the caches are
+    flushed before every call, outside the events."""
+    fn()
+    ev = []
+    for _ in range(reps):
+        if flush:
+            flush()
+        e0, e1 = events(torch)
+        e0.record()
+        fn()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def run_probes(torch, dev, reps=10):
+    """HBM stream ceilings (read, write, copy: 1 GiB cold, and the step's
+    access pattern of four 64 MiB tensors in rotation) and VALU issue rates."""
+    L = probe_lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = cu_count(torch)
+    out = {"hbm": {}, "valu": {}}
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    small = torch.empty(64 * cus * 256, dtype=torch.int32, device=dev)
+    flush = Flusher(torch, dev)
+
+    def stream_call(kind, src, dst, nbytes, grid):
+        def fn():
+            if L.fp4q_probe_stream(kind, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                   nbytes // 16, grid, stream) != 0:
+                raise RuntimeError("probe stream failed")
+        return fn
+
+    for name, kind, moved in (("read, 4 loads in flight", 0, 1), ("read, 8 loads in flight", 4, 1),
+                              ("read, 16 loads in flight", 5, 1), ("read, 8 non-temporal loads in flight", 6, 1),
+                              ("write (streaming stores)", 1, 1), ("write (plain stores)", 7, 1),
+                              ("copy (streaming stores)", 2, 2), ("copy (streaming stores, 8 loads in flight)", 8, 2),
+                              ("copy (plain stores)", 3, 2)):
+        best = None
+        for wpc in (4, 8, 16, 32):
+            grid = wpc * cus
+            dst = small if kind in (0, 4, 5, 6) else b
+            ms = time_fn(torch, stream_call(kind, a, dst, n, grid), reps, flush)
+            gbs = moved * n / (ms * 1e6)
+            if best is None or gbs > best["GB/s"]:
+                best = {"GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "ms": round(ms, 4),
+                        "workgroups": grid}
+        out["hbm"][f"{name}, 1 GiB, cold"] = best
+    # the step's pattern: four 64 MiB inputs in rotation, copied into four outputs
+    xs = [torch.ones(16 << 20, dtype=torch.float32, device=dev) for _ in range(4)]
+    ys = [torch.empty_like(x) for x in xs]
+    grid = 8 * cus
+    ev = []
+    for i in range(36):
+        e0, e1 = events(torch)
+        e0.record()
+        if L.fp4q_probe_stream(2, ctypes.c_void_p(xs[i % 4].data_ptr()), ctypes.c_void_p(ys[(i + 1) % 4].data_ptr()),
+                               (64 << 20) // 16, grid, stream) != 0:
+            raise RuntimeError("probe stream failed")
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([p.elapsed_time(q) for p, q in ev[4:]]))
+    gbs = 2 * (64 << 20) / (ms * 1e6)
+    out["hbm"]["copy (streaming stores), four 64 MiB tensors in rotation, warm"] = {
+        "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "ms": round(ms, 4), "workgroups": grid}
+    del a, b, xs, ys, flush
+
+    o = torch.empty(32 * cus * 256, dtype=torch.float32, device=dev)
+    for kind, name in VALU_PROBES.items():
+        iters = 4096 if kind < 5 else 1024
+        grid = 32 * cus
+
+        def fn(kind=kind, iters=iters, grid=grid):
+            if L.fp4q_probe_valu(kind, iters, grid, ctypes.c_void_p(o.data_ptr()), stream) != 0:
+                raise RuntimeError("probe valu failed")
+        ms = time_fn(torch, fn, reps)
+        out["valu"][name] = {"kind": kind, "iters": iters, "workgroups": grid, "ms": round(ms, 5),
+                             "lanes": grid * 256}
+    return out
+
+
+# --------------------------------------------------------------------------
+# the step: the fp32 4096 x 4096 block-size sweep
+# --------------------------------------------------------------------------
+
+class Builder:
+    """Preallocated outputs of library calls (kept alive with the inputs)."""
+
+    def __init__(self, F, torch, dev):
+        self.F, self.torch, self.dev = F, torch, dev
+        self.keep = []
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def empty(self, shape, dtype):
+        t = self.torch.empty(shape, dtype=dtype, device=self.dev)
+        self.keep.append(t)
+        return t
+
+    @staticmethod
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+    def quantize_call(self, name, cfg, x, x_dt, kind, meta, dq_dt=None, mse=True):
+        """fp4q_quantize of x [R, C] with every requested output preallocated."""
+        F, torch = self.F, self.torch
+        self.keep.append(cfg)
+        R, C = x.shape
+        B = cfg.block
+        codes = self.empty((R, C // 2), torch.uint8)
+        scales = self.empty((R, C // B), torch.uint8)
+        g = self.empty((1,), torch.float32)
+        dq = None if dq_dt is None else self.empty((R, C), {F.F32: torch.float32, F.BF16: torch.bfloat16}[dq_dt])
+        m = self.empty((R, C // B), torch.float32) if mse else None
+        ws = self.empty((max(F.workspace_bytes(cfg, R, C), 16),), torch.uint8)
+        args = (ctypes.byref(cfg), self.ptr(x), x_dt, R, C, C, self.ptr(codes), self.ptr(scales), self.ptr(g),
+                self.ptr(dq), dq_dt if dq_dt is not None else F.F32, C, self.ptr(m), self.ptr(ws), self.stream)
+        in_es = 4 if x_dt == F.F32 else 2
+        dq_es = 0 if dq_dt is None else (4 if dq_dt == F.F32 else 2)
+        nbytes = quant_bytes(R, C, B, in_es, dq_es, mse=mse, dq=dq_dt is not None)
+        c = Call(name, F.lib().fp4q_quantize, args, nbytes, R * C, kind, meta)
+        c.outputs = dict(codes=codes, scales=scales, g=g)
+        return c
+
+
 def build_step(F, S, torch, dev):
     """Generate the workload on the host, upload it, preallocate every output."""
     L = F.lib()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    bld = Builder(F, torch, dev)
     host = S.config2()
     names = ["normal", "laplace", "normal_1e-4", "laplace_1e-4"]
     R, C = host["normal"].shape
     X = {k: S.to_torch(host[k], S.F32, dev) for k in names}
-    keep = list(X.values())                      # keep tensors and configs alive
-
-    def t_empty(shape, dtype):
-        t = torch.empty(shape, dtype=dtype, device=dev)
-        keep.append(t)
-        return t
-
-    def ptr(t):
-        return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    bld.keep += list(X.values())
+    ptr = bld.ptr
 
     calls = []
     combos = [(B, st, gm) for B in (4, 8, 16, 32) for st in (0, 1, 2, 3) for gm in (1, 0)]
     for ci, (B, st, gm) in enumerate(combos):
         for ti in range(4):
             tname = names[(ti + ci) % 4]       # every combo on all four tensors, rotated per combo
-            x = X[tname]
             cfg = F.config(F.E4M3, B, st, gm)
-            keep.append(cfg)
-            codes = t_empty((R, C // 2), torch.uint8)
-            scales = t_empty((R, C // B), torch.uint8)
-            g = t_empty((1,), torch.float32)
-            dq = t_empty((R, C), torch.float32)
-            mse = t_empty((R, C // B), torch.float32)
-            ws = t_empty((max(F.workspace_bytes(cfg, R, C), 16),), torch.uint8)
-            args = (ctypes.byref(cfg), ptr(x), F.F32, R, C, C, ptr(codes), ptr(scales), ptr(g), ptr(dq),
-                    F.F32, C, ptr(mse), ptr(ws), stream)
-            calls.append(Call(f"quantize B={B} {STRATS[st]} {'amax' if gm else 'none'}", L.fp4q_quantize, args,
-                              quant_bytes(R, C, B), R * C, "quantize",
-                              dict(B=B, strategy=STRATS[st], global_mode="tensor-amax" if gm else "none",
-                                   tensor=tname)))
+            calls.append(bld.quantize_call(f"quantize B={B} {STRATS[st]} {'amax' if gm else 'none'}", cfg, X[tname],
+                                           F.F32, "quantize",
+                                           dict(B=B, strategy=STRATS[st], global_mode="tensor-amax" if gm else "none",
+                                                tensor=tname), dq_dt=F.F32))
 
     xn = X["normal"]
     # block Hadamard fused before quantization
     for H, cfg in ((16, F.nvfp4(0, hadamard=16)), (32, F.mxfp4(0, hadamard=32))):
-        keep.append(cfg)
-        codes = t_empty((R, C // 2), torch.uint8)
-        scales = t_empty((R, C // cfg.block), torch.uint8)
-        g = t_empty((1,), torch.float32)
-        dq = t_empty((R, C), torch.float32)
-        mse = t_empty((R, C // cfg.block), torch.float32)
-        ws = t_empty((max(F.workspace_bytes(cfg, R, C), 16),), torch.uint8)
-        args = (ctypes.byref(cfg), ptr(xn), F.F32, R, C, C, ptr(codes), ptr(scales), ptr(g), ptr(dq), F.F32, C,
-                ptr(mse), ptr(ws), stream)
-        calls.append(Call(f"quantize hadamard={H} {'nvfp4' if H == 16 else 'mxfp4'}", L.fp4q_quantize, args,
-                          quant_bytes(R, C, cfg.block), R * C, "rotate+quantize", dict(H=H)))
+        c = bld.quantize_call(f"quantize hadamard={H} {'nvfp4' if H == 16 else 'mxfp4'}", cfg, xn, F.F32,
+                              "rotate+quantize", dict(H=H), dq_dt=F.F32)
+        calls.append(c)
         if H == 16:
-            nv_codes, nv_scales, nv_g, nv_cfg = codes, scales, g, cfg
+            nv, nv_cfg = c.outputs, cfg
 
     # stand-alone dequantize and block MSE of the NVFP4 (rotated) result
-    out = t_empty((R, C), torch.float32)
+    out = bld.empty((R, C), torch.float32)
     calls.append(Call("dequantize nvfp4", L.fp4q_dequantize,
-                      (ctypes.byref(nv_cfg), ptr(nv_codes), ptr(nv_scales), ptr(nv_g), R, C, ptr(out), F.F32, C, stream),
+                      (ctypes.byref(nv_cfg), ptr(nv["codes"]), ptr(nv["scales"]), ptr(nv["g"]), R, C, ptr(out), F.F32,
+                       C, bld.stream),
                       R * C // 2 + R * C // 16 + 4 * R * C, R * C, "dequantize", {}))
-    mse = t_empty((R, C // 16), torch.float32)
+    mse = bld.empty((R, C // 16), torch.float32)
     calls.append(Call("block_mse nvfp4", L.fp4q_block_mse,
-                      (ctypes.byref(nv_cfg), ptr(xn), F.F32, R, C, C, ptr(nv_codes), ptr(nv_scales), ptr(nv_g),
-                       ptr(mse), stream),
+                      (ctypes.byref(nv_cfg), ptr(xn), F.F32, R, C, C, ptr(nv["codes"]), ptr(nv["scales"]),
+                       ptr(nv["g"]), ptr(mse), bld.stream),
                       4 * R * C + R * C // 2 + R * C // 16 + 4 * R * C // 16, R * C, "block_mse", {}))
 
     # FOCUS relaxed fake-quant forward / backward, sub-blocks of 8
@@ -310,69 +517,146 @@ def build_step(F, S, torch, dev):
     c16 = S.cast(rng.uniform(0.8, 1.25, (R, C // K)), S.F16)
     ct = S.to_torch(c16, S.F16, dev)
     gt = S.to_torch(S.normal(R, C, 8, S.F32), S.F32, dev)
-    keep += [ct, gt]
+    bld.keep += [ct, gt]
     for cfg in (F.mxfp4(), F.nvfp4(0, F.GLOBAL_USER, 2.0 ** -12)):
-        keep.append(cfg)
-        B = cfg.block
-        scales = t_empty((R, C // B), torch.uint8)
-        gq = t_empty((1,), torch.float32)
-        codes = t_empty((R, C // 2), torch.uint8)
-        ws = t_empty((16,), torch.uint8)
-        # S_dq from abs-max quantization (outside the timed step)
-        st = L.fp4q_quantize(ctypes.byref(cfg), ptr(xn), F.F32, R, C, C, ptr(codes), ptr(scales), ptr(gq),
-                             None, F.F32, C, None, ptr(ws), stream)
-        assert st == 0, st
-        g_in = None if cfg.scale_fmt == F.E8M0 else gq
-        w_hat = t_empty((R, C), torch.float32)
-        fcodes = t_empty((R, C // 2), torch.uint8)
-        grad_c = t_empty((R, C // K), torch.float32)
-        fmt = "mxfp4" if B == 32 else "nvfp4"
-        calls.append(Call(f"focus fwd {fmt}", L.fp4q_relaxed_fakequant_fwd,
-                          (ctypes.byref(cfg), ptr(xn), F.F32, R, C, C, ptr(scales), ptr(g_in), ptr(ct), K,
-                           ptr(w_hat), F.F32, C, ptr(fcodes), stream),
-                          4 * R * C + 2 * R * C // K + R * C // B + 4 * R * C + R * C // 2, R * C, "focus_fwd", {}))
-        calls.append(Call(f"focus bwd {fmt}", L.fp4q_relaxed_fakequant_bwd,
-                          (ctypes.byref(cfg), ptr(xn), F.F32, R, C, C, ptr(scales), ptr(g_in), ptr(ct), K, ptr(gt),
-                           F.F32, C, ptr(grad_c), stream),
-                          8 * R * C + 2 * R * C // K + R * C // B + 4 * R * C // K, R * C, "focus_bwd", {}))
+        calls += focus_calls(F, bld, cfg, xn, F.F32, ct, gt, F.F32, K, F.F32, "", codes=True)
     torch.cuda.synchronize()
-    return calls, keep, host, X
+    return calls, bld, host, X
+
+
+def focus_calls(F, bld, cfg, w, w_dt, ct, gt, g_dt, K, out_dt, tag, codes=True):
+    """FOCUS forward (+ codes) and backward calls with S_dq from an abs-max
+    quantization of w (made here, outside any timing)."""
+    torch = bld.torch
+    L = F.lib()
+    ptr = bld.ptr
+    bld.keep.append(cfg)
+    R, C = w.shape
+    B = cfg.block
+    scales = bld.empty((R, C // B), torch.uint8)
+    gq = bld.empty((1,), torch.float32)
+    qc = bld.empty((R, C // 2), torch.uint8)
+    ws = bld.empty((max(F.workspace_bytes(cfg, R, C), 16),), torch.uint8)
+    st = L.fp4q_quantize(ctypes.byref(cfg), ptr(w), w_dt, R, C, C, ptr(qc), ptr(scales), ptr(gq), None, F.F32, C,
+                         None, ptr(ws), bld.stream)
+    assert st == 0, st
+    g_in = None if cfg.scale_fmt == F.E8M0 else gq
+    es = 4 if w_dt == F.F32 else 2
+    oes = 4 if out_dt == F.F32 else 2
+    w_hat = bld.empty((R, C), torch.float32 if out_dt == F.F32 else torch.bfloat16)
+    fcodes = bld.empty((R, C // 2), torch.uint8) if codes else None
+    grad_c = bld.empty((R, C // K), torch.float32)
+    fmt = "mxfp4" if B == 32 else "nvfp4"
+    fwd_bytes = es * R * C + 2 * R * C // K + R * C // B + oes * R * C + (R * C // 2 if codes else 0)
+    bwd_bytes = es * R * C + (4 if g_dt == F.F32 else 2) * R * C + 2 * R * C // K + R * C // B + 4 * R * C // K
+    return [Call(f"focus fwd {fmt}{tag}", L.fp4q_relaxed_fakequant_fwd,
+                 (ctypes.byref(cfg), ptr(w), w_dt, R, C, C, ptr(scales), ptr(g_in), ptr(ct), K,
+                  ptr(w_hat), out_dt, C, ptr(fcodes), bld.stream), fwd_bytes, R * C, "focus_fwd", {"fmt": fmt}),
+            Call(f"focus bwd {fmt}{tag}", L.fp4q_relaxed_fakequant_bwd,
+                 (ctypes.byref(cfg), ptr(w), w_dt, R, C, C, ptr(scales), ptr(g_in), ptr(ct), K, ptr(gt),
+                  g_dt, C, ptr(grad_c), bld.stream), bwd_bytes, R * C, "focus_bwd", {"fmt": fmt})]
+
+
+# --------------------------------------------------------------------------
+# the other workloads, per call
+# --------------------------------------------------------------------------
+
+def build_configs(F, S, torch, dev):
+    """Preallocated calls of the fp32 1024^2, Llama-shaped weight, activation
+    and FOCUS workloads: {config label: (description, [calls])}."""
+    bld = Builder(F, torch, dev)
+    out = {}
+
+    x1 = S.to_torch(S.config1(), S.F32, dev)
+    bld.keep.append(x1)
+    out["C1"] = ("fp32 1024x1024 N(0,1): MXFP4 and NVFP4 abs-max, every output (launch-bound; reported, not "
+                 "judged against the roofline)",
+                 [bld.quantize_call("C1 mxfp4 absmax", F.mxfp4(), x1, F.F32, "quantize", {}, dq_dt=F.F32),
+                  bld.quantize_call("C1 nvfp4 absmax amax", F.nvfp4(), x1, F.F32, "quantize", {}, dq_dt=F.F32)])
+
+    c3 = S.config3()
+    calls = []
+    for wname in ("w_down", "w_up"):
+        w = S.to_torch(c3[wname], S.BF16, dev)
+        bld.keep.append(w)
+        shape = "x".join(map(str, w.shape))
+        for fname, mk in (("nvfp4 4-over-6 amax", lambda: F.nvfp4(F.FOUR_OVER_SIX)), ("mxfp4 absmax", F.mxfp4)):
+            for full in (False, True):
+                mode = "full" if full else "packed"
+                calls.append(bld.quantize_call(f"C3 {wname} {shape} {fname} {mode}", mk(), w, F.BF16, "quantize",
+                                               {"mode": mode}, dq_dt=F.BF16 if full else None, mse=full))
+    del c3
+    out["C3"] = ("Llama-3.1-8B-shaped bf16 MLP weights (W_down 4096x14336, W_gate/up 14336x4096; 0.02 Student-t "
+                 "df=3, 0.5% of columns x20): NVFP4 4-over-6 + tensor-amax and MXFP4 abs-max; packed-only "
+                 "(codes + scales) and full (+ bf16 dequant + block MSE)", calls)
+
+    a = S.to_torch(S.config4(), S.BF16, dev)
+    bld.keep.append(a)
+    calls = []
+    acts = (("mxfp4 absmax", lambda H: F.mxfp4(hadamard=H)),
+            ("nvfp4 absmax amax", lambda H: F.nvfp4(hadamard=H)),
+            ("nvfp4 absmax user-g", lambda H: F.nvfp4(global_mode=F.GLOBAL_USER, global_scale=0.015625, hadamard=H)),
+            ("nvfp4 4-over-6 amax", lambda H: F.nvfp4(F.FOUR_OVER_SIX, hadamard=H)))
+    for H in (0, 16, 32):
+        for fname, mk in acts:
+            for full in (False, True):
+                mode = "full" if full else "packed"
+                calls.append(bld.quantize_call(f"C4 H={H} {fname} {mode}", mk(H), a, F.BF16, "quantize",
+                                               {"H": H, "mode": mode}, dq_dt=F.BF16 if full else None, mse=full))
+    out["C4"] = ("bf16 activations 8192x4096 (Laplace(0,1), 0.1% of channels x50), block Hadamard H in {0, 16, 32} "
+                 "fused before MXFP4 / NVFP4 (tensor-amax pre-pass over the rotated rows, or a user g) quantization; "
+                 "packed-only and full outputs", calls)
+
+    K = 8
+    w5, c5, g5 = S.config5(K)
+    wt, ct, gt = S.to_torch(w5, S.BF16, dev), S.to_torch(c5, S.F16, dev), S.to_torch(g5, S.BF16, dev)
+    bld.keep += [wt, ct, gt]
+    calls = []
+    for cfg in (F.mxfp4(), F.nvfp4()):
+        calls += focus_calls(F, bld, cfg, wt, F.BF16, ct, gt, F.BF16, K, F.BF16, "", codes=False)
+        calls += focus_calls(F, bld, cfg, wt, F.BF16, ct, gt, F.BF16, K, F.BF16, " +codes", codes=True)[:1]
+    out["C5"] = ("FOCUS fake-quant of bf16 4096x12288 N(0,0.02) weights, sub-blocks of 8, fp16 c ~ U[0.8,1.25], "
+                 "bf16 upstream gradient N(0,1); S_dq from MXFP4 / NVFP4 abs-max; forward (bf16 W_hat, with and "
+                 "without codes) and STE backward (fp32 grad_c)", calls)
+    torch.cuda.synchronize()
+    return out, bld
+
+
+def time_configs(torch, configs, flush, reps_warm=10, reps_cold=5):
+    res = {}
+    for label, (what, calls) in configs.items():
+        rows = {}
+        tb = tw = tc = 0.0
+        for c in calls:
+            mw = time_fn(torch, c, reps_warm)
+            mc = time_fn(torch, c, reps_cold, flush)
+            gw, gc = c.nbytes / (mw * 1e6), c.nbytes / (mc * 1e6)
+            rows[c.name] = {"bytes": c.nbytes, "ms_warm": round(mw, 4), "GB/s_warm": round(gw, 1),
+                            "hbm_frac_warm": round(gw / HBM_PEAK_GBS, 4), "ms_cold": round(mc, 4),
+                            "GB/s_cold": round(gc, 1), "hbm_frac_cold": round(gc / HBM_PEAK_GBS, 4),
+                            "Gelem/s_cold": round(c.elems / (mc * 1e6), 2)}
+            tb += c.nbytes
+            tw += mw
+            tc += mc
+        res[label] = {"what": what, "GB/s_warm": round(tb / (tw * 1e6), 1),
+                      "hbm_frac_warm": round(tb / (tw * 1e6) / HBM_PEAK_GBS, 4),
+                      "GB/s_cold": round(tb / (tc * 1e6), 1), "hbm_frac_cold": round(tb / (tc * 1e6) / HBM_PEAK_GBS, 4),
+                      "calls": rows}
+    return res
 
 
 def time_quantize_configs(F, torch, x, cfgs, reps=5):
     """Quantize calls outside the step (widenings of the path): each config on
     one 4096 x 4096 fp32 input with every output, timed per call with HIP
     events on the library's stream; GB/s of the call's algorithmic bytes."""
-    L = F.lib()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    bld = Builder(F, torch, x.device)
     R, C = x.shape
     out = {}
     for name, cfg in cfgs:
-        B = cfg.block
-        codes = torch.empty((R, C // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((R, C // B), dtype=torch.uint8, device=x.device)
-        g = torch.empty(1, dtype=torch.float32, device=x.device)
-        dq = torch.empty((R, C), dtype=torch.float32, device=x.device)
-        mse = torch.empty((R, C // B), dtype=torch.float32, device=x.device)
-        ws = torch.empty(max(F.workspace_bytes(cfg, R, C), 16), dtype=torch.uint8, device=x.device)
-        args = (ctypes.byref(cfg), ctypes.c_void_p(x.data_ptr()), F.F32, R, C, C, ctypes.c_void_p(codes.data_ptr()),
-                ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(dq.data_ptr()),
-                F.F32, C, ctypes.c_void_p(mse.data_ptr()), ctypes.c_void_p(ws.data_ptr()), stream)
-        ev = []
-        for i in range(reps + 1):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            st_ = L.fp4q_quantize(*args)
-            e1.record()
-            if st_ != 0:
-                raise RuntimeError(f"{name}: status {st_}")
-            ev.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[1:]]))
-        nb = quant_bytes(R, C, B)
-        out[name] = {"ms": round(ms, 4), "GB/s": round(nb / (ms * 1e6), 1),
-                     "Gelem/s": round(R * C / (ms * 1e6), 2), "g": float(g.item())}
+        c = bld.quantize_call(name, cfg, x, F.F32, "quantize", {}, dq_dt=F.F32)
+        ms = time_fn(torch, c, reps)
+        out[name] = {"ms": round(ms, 4), "GB/s": round(c.nbytes / (ms * 1e6), 1),
+                     "Gelem/s": round(R * C / (ms * 1e6), 2), "g": float(c.outputs["g"].item())}
     return out
 
 
@@ -384,19 +668,13 @@ def time_histogram(F, torch, x, reps=10):
     R, C = x.shape
     codes = F.quantize(x, F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_NONE), want_mse=False)["codes"]
     counts = torch.zeros(16, dtype=torch.int64, device=x.device)
-    ev = []
-    for _ in range(reps + 1):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
+
+    def fn():
         st_ = L.fp4q_code_histogram(ctypes.c_void_p(codes.data_ptr()), R, C, ctypes.c_void_p(counts.data_ptr()),
                                     stream)
-        e1.record()
         if st_ != 0:
             raise RuntimeError(f"histogram: status {st_}")
-        ev.append((e0, e1))
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev[1:]]))
+    ms = time_fn(torch, fn, reps)
     h = counts.cpu().numpy() / (reps + 1)                 # the calls accumulate
     return {"ms": round(ms, 4), "GB/s": round(R * C / 2 / (ms * 1e6), 1),
             "zero_code_fraction": round(float(h[0] + h[8]) / (R * C), 4),
@@ -423,16 +701,7 @@ def time_gemm(F, torch, dev, warm=30, reps=10, rounds=3):
         args = (qa["codes"], qa["scales"], qb["codes"], qb["scales"], c, ws)
         for _ in range(warm):
             F.fp4q_mxfp4_gemm(*args)
-        ev = []
-        for _ in range(rounds * reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            F.fp4q_mxfp4_gemm(*args)
-            e1.record()
-            ev.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        ms = time_fn(torch, lambda: F.fp4q_mxfp4_gemm(*args), rounds * reps)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         out[f"{M}x{N}x{K}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
                                "mfma_frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4)}
@@ -465,20 +734,23 @@ def time_gemm(F, torch, dev, warm=30, reps=10, rounds=3):
     return out
 
 
-def cpu_baseline(O, S, host, rows_per_tensor):
-    """The oracle (single thread) on the first rows of every tensor, over the
-    same call list as one GPU step."""
+# --------------------------------------------------------------------------
+# the oracle on the host cores
+# --------------------------------------------------------------------------
+
+def cpu_step_sample(O, S, host, r0, r1):
+    """The step's call list on rows [r0, r1) of every tensor, through the
+    single-threaded oracle; returns the algorithmic bytes."""
     names = ["normal", "laplace", "normal_1e-4", "laplace_1e-4"]
     nbytes = 0
-    t0 = time.perf_counter()
     for B in (4, 8, 16, 32):
         for st in (0, 1, 2, 3):
             for gm in (1, 0):
                 for name in names:
-                    x = np.ascontiguousarray(host[name][:rows_per_tensor])
+                    x = np.ascontiguousarray(host[name][r0:r1])
                     O.quantize(x, fmt=1, block=B, strategy=st, global_mode=gm)
                     nbytes += quant_bytes(x.shape[0], x.shape[1], B)
-    x = np.ascontiguousarray(host["normal"][:rows_per_tensor])
+    x = np.ascontiguousarray(host["normal"][r0:r1])
     r, c = x.shape
     for H, fmt, B, gm in ((16, 1, 16, 1), (32, 0, 32, 0)):
         q = O.quantize(x, fmt=fmt, block=B, strategy=0, global_mode=gm, hadamard=H)
@@ -495,14 +767,142 @@ def cpu_baseline(O, S, host, rows_per_tensor):
         O.relaxed_bwd(x, q["scales"], g, c16, gr, fmt=fmt, block=B, sub_block=8)
         nbytes += 8 * r * c + r * c // 4 + r * c // B + r * c // 2
         nbytes += 8 * r * c + r * c // 4 + r * c // B + r * c // 2
-    dt = time.perf_counter() - t0
-    return nbytes, dt
+    return nbytes
 
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(O, S, host, rows):
+    """The oracle (its plain single-threaded C) over the step's call list on a
+    bounded row sample: (i) one thread pinned to one core on rows [0, rows);
+    (ii) every core of this process's CPU set (at most 16), each thread on its
+    own rows of the same tensors, concurrently (ctypes releases the GIL)."""
+    cores = sorted(os.sched_getaffinity(0))
+    O.lib()
+    os.sched_setaffinity(0, {cores[0]})
+    try:
+        t0 = time.perf_counter()
+        nb1 = cpu_step_sample(O, S, host, 0, rows)
+        dt1 = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, set(cores))
+    n = min(len(cores), 16)
+    per = max(1, rows // 4)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(n) as ex:
+        nbn = sum(ex.map(lambda i: cpu_step_sample(O, S, host, rows + i * per, rows + (i + 1) * per), range(n)))
+    dtn = time.perf_counter() - t0
+    return {"value": round(nb1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the step's call list on the first {rows} rows of each 4096x4096 tensor "
+                      f"({nb1 / 1e6:.1f} MB algorithmic, {dt1:.1f} s, one thread pinned to one core)",
+            "all_cores": {"value": round(nbn / dtn / 1e9, 4), "unit": "GB/s", "cores": n,
+                          "sample": f"{n} threads, each the step's call list on its own {per} rows "
+                                    f"({nbn / 1e6:.1f} MB algorithmic, {dtn:.1f} s)"},
+            "cpu_model": cpu_model(), "host_cpus_visible": len(cores),
+            "compiler": "gcc " + " ".join(O.CFLAGS)}
+
+
+# --------------------------------------------------------------------------
+# roofline of the dominant kernel
+# --------------------------------------------------------------------------
+
+def profiled_calls(calls, prof):
+    """The calls a bench.py --only profiling run made, in dispatch order (its
+    pattern is read from the command recorded with the profile)."""
+    import re
+    m = re.search(r"--only '([^']*)'", prof.get("command", "")) if prof else None
+    pats = m.group(1).split("|") if m else []
+    return [c for c in calls if any(p in c.name for p in pats)]
+
+
+def bf_roofline(calls, per_call, dom, B, valu_probe):
+    """Roofline of the brute-force quantize kernel over its launches without
+    the abs-max pre-pass (their HIP events hold the kernel alone): executed
+    VALU lane-instructions (SQ_INSTS_VALU x 64 per dispatch, from the
+    committed counter profile of the same calls on the same sources) over
+    the live mean launch time, against the fp32 vector peak."""
+    kname = f"k_quant_bf<float, {B}, 0, 1>"
+    prof = load_profile("counters_bench_dominant")
+    kc = kernel_counters(prof, kname)
+    solo = [(c, ms) for c, ms in dom if c.meta.get("global_mode") == "none"]
+    ms_solo = float(np.mean([ms for _, ms in solo]))
+    roof = {"bound": "alu", "kernel": kname, "achieved": None, "peak": round(VALU_PEAK_TOPS, 1),
+            "unit": "T VALU lane-instructions/s", "frac": None, "traffic": None,
+            "avg_launch_ms": round(ms_solo, 4), "launches": f"{len(solo)} per step (the calls without the "
+                                                           "per-tensor pre-pass, whose events time this kernel alone)",
+            "work": "executed VALU lane-instructions per launch = SQ_INSTS_VALU x 64 (rocprofv3 counters of the "
+                    "same calls on the same kernel sources, profiles/counters_bench_dominant)",
+            "algorithmic_MB_per_launch": round(dom[0][0].nbytes / 1e6, 2)}
+    elems = dom[0][0].elems
+    exhaustive = BF_CANDIDATES * BF_INSTR_PER_EVAL * elems
+    roof["exhaustive_equivalent"] = {
+        "value": round(exhaustive / (ms_solo * 1e-3) / 1e12, 2), "unit": "T lane-instructions/s",
+        "what": f"{BF_CANDIDATES} candidates x {BF_INSTR_PER_EVAL} VALU instructions x {elems} elements per launch "
+                "(an exhaustive search) / time; the exact branch and bound evaluates a fraction of the candidates"}
+    if valu_probe:
+        roof["valu_probe"] = valu_probe
+    if not kc or "SQ_INSTS_VALU" not in kc or "values" not in kc["SQ_INSTS_VALU"]:
+        roof["why_null"] = "no per-dispatch counter profile on the current kernel sources"
+        return roof
+    seq = [c for c in profiled_calls(calls, prof) if c.meta.get("strategy") == "brute-force" and c.meta.get("B") == B]
+    vals = kc["SQ_INSTS_VALU"]["values"]
+    if not seq or len(vals) % len(seq):
+        roof["why_null"] = "the counter profile's dispatches do not match its calls"
+        return roof
+    ins_of = {id(c): 64.0 * float(np.mean(vals[k::len(seq)])) for k, c in enumerate(seq)}
+    if any(id(c) not in ins_of for c, _ in solo):
+        roof["why_null"] = "the counter profile does not cover every launch"
+        return roof
+    total_instr = sum(ins_of[id(c)] for c, _ in solo)
+    total_ms = sum(ms for _, ms in solo)
+    achieved = total_instr / (total_ms * 1e-3) / 1e12
+    roof["achieved"] = round(achieved, 2)
+    roof["frac"] = round(achieved / VALU_PEAK_TOPS, 4)
+    roof["executed_valu_lane_instr_per_launch"] = round(total_instr / len(solo))
+    groups = {}
+    for c, ms in solo:
+        key = "x1e-4 tensors (no per-tensor scale: block scales underflow, short searches)" \
+            if c.meta.get("tensor", "").endswith("1e-4") else "N(0,1) and Laplace(0,1) tensors"
+        g = groups.setdefault(key, [0.0, 0.0, 0])
+        g[0] += ins_of[id(c)]
+        g[1] += ms
+        g[2] += 1
+    roof["by_input"] = {k: {"launches": v[2], "avg_launch_ms": round(v[1] / v[2], 4),
+                            "executed_lane_instr_per_launch": round(v[0] / v[2]),
+                            "achieved": round(v[0] / (v[1] * 1e-3) / 1e12, 2),
+                            "frac": round(v[0] / (v[1] * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4)}
+                        for k, v in groups.items()}
+    tr = copy_scaled_traffic(prof, kc)
+    if tr:
+        roof["traffic"] = round(float(np.mean(tr)) / 1e6, 2)
+        roof["traffic_unit"] = "MB per launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size)"
+    return roof
+
+
+def valu_probe_summary():
+    """Executed-instruction rates of the VALU probes from the committed probe
+    profile (kernel time and SQ_INSTS_VALU of the same run)."""
+    prof = json.load(open(os.path.join(PROFILES, "valu_probe.json"))) if os.path.exists(
+        os.path.join(PROFILES, "valu_probe.json")) else None
+    if not prof or "rates" not in prof:
+        return None
+    return {"measured_T_lane_instr_per_s": prof["rates"], "source": "profiles/valu_probe.md"}
+
+
+# --------------------------------------------------------------------------
 
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize, args.label or "profile", args.command)
+        summarize(args.summarize, args.label or "profile", args.command, args.probe_json)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no multi-GPU "
@@ -516,6 +916,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.probe:
+        print("[bench] probes", file=sys.stderr, flush=True)
+        res = run_probes(torch, dev)
+        print(json.dumps(res), flush=True)
+        if args.json_out:
+            with open(args.json_out, "w") as f:
+                f.write(json.dumps(res) + "\n")
+        return
     if args.profile_gemm:
         gen = torch.Generator(device=dev).manual_seed(11)
         M = N = K = 8192
@@ -536,27 +944,28 @@ def main():
         torch.cuda.synchronize()
         print("[bench] profiling run done", file=sys.stderr, flush=True)
         return
+    if args.configs_only is not None:
+        configs, _cbld = build_configs(F, S, torch, dev)
+        pats = args.configs_only.split("|")
+        sel = [c for _, calls in configs.values() for c in calls if any(pt in c.name for pt in pats)]
+        print(f"[bench] profiling {len(sel)} calls x {args.steps}: {[c.name for c in sel][:6]}", file=sys.stderr,
+              flush=True)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            for c in sel:
+                c()
+        torch.cuda.synchronize()
+        print("[bench] profiling run done", file=sys.stderr, flush=True)
+        return
     print("[bench] generating and uploading the workload", file=sys.stderr, flush=True)
-    calls, keep, host, X = build_step(F, S, torch, dev)
+    calls, bld, host, X = build_step(F, S, torch, dev)
     step_bytes = sum(c.nbytes for c in calls)
-
-    def step(record=False):
-        for c in calls:
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                c()
-                e1.record()
-                c.times.append((e0, e1))
-            else:
-                c()
 
     if args.only is not None or args.copy_mb:
         pats = [] if args.only is None else args.only.split("|")
         sel = [c for c in calls if any(pt in c.name for pt in pats)]
-        print(f"[bench] profiling {len(sel)} calls x {args.steps}: {[c.name for c in sel][:4]}", file=sys.stderr,
-              flush=True)
+        print(f"[bench] profiling {len(sel)} calls x {args.steps}: {[(c.name, c.meta.get('tensor')) for c in sel][:8]}",
+              file=sys.stderr, flush=True)
         if args.copy_mb:
             src = torch.empty(args.copy_mb << 18, dtype=torch.float32, device=dev)
             dst = torch.empty_like(src)
@@ -570,6 +979,17 @@ def main():
         torch.cuda.synchronize()
         print("[bench] profiling run done", file=sys.stderr, flush=True)
         return
+
+    def step(record=False):
+        for c in calls:
+            if record:
+                e0, e1 = events(torch)
+                e0.record()
+                c()
+                e1.record()
+                c.times.append((e0, e1))
+            else:
+                c()
 
     print(f"[bench] {len(calls)} calls per step, warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -591,17 +1011,32 @@ def main():
         ms = float(np.mean([a.elapsed_time(b) for a, b in c.times]))
         per_call.append((c, ms))
 
-    # per-strategy aggregates (quantize calls)
+    # cold leg: every call once more, each after a cache flush outside its events
+    flush = Flusher(torch, dev)
+    for c in calls:
+        flush()
+        e0, e1 = events(torch)
+        e0.record()
+        c()
+        e1.record()
+        c.cold.append((e0, e1))
+    torch.cuda.synchronize()
+    cold_ms = {id(c): float(np.mean([a.elapsed_time(b) for a, b in c.cold])) for c in calls}
+    print(f"[bench] cold leg: {sum(cold_ms.values()):.3f} ms of calls", file=sys.stderr, flush=True)
+
+    # per-strategy aggregates
     groups = {}
     for c, ms in per_call:
         key = c.meta.get("strategy", c.kind)
-        g = groups.setdefault(key, [0, 0, 0.0])
+        g = groups.setdefault(key, [0, 0, 0.0, 0.0])
         g[0] += c.nbytes
         g[1] += c.elems
         g[2] += ms
+        g[3] += cold_ms[id(c)]
     breakdown = {k: {"GB/s": round(b / (ms * 1e6), 1), "Gelem/s": round(e / (ms * 1e6), 2),
-                     "hbm_frac": round(b / (ms * 1e6) / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4)}
-                 for k, (b, e, ms) in groups.items()}
+                     "hbm_frac": round(b / (ms * 1e6) / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4),
+                     "GB/s_cold": round(b / (cms * 1e6), 1), "hbm_frac_cold": round(b / (cms * 1e6) / HBM_PEAK_GBS, 4)}
+                 for k, (b, e, ms, cms) in groups.items()}
 
     # dominant kernel: the kernel family (strategy, block) with the largest share of the step
     fam = {}
@@ -610,57 +1045,37 @@ def main():
         fam.setdefault(key, []).append((c, ms))
     dom_key = max(fam, key=lambda k: sum(ms for _, ms in fam[k]))
     dom = fam[dom_key]
-    solo = [(c, ms) for c, ms in dom if c.meta.get("global_mode") != "tensor-amax"] or dom
-    dom_ms = float(np.mean([ms for _, ms in solo]))    # launches without the abs-max pre-pass
-    dom_elems = dom[0][0].elems
     strategy, B = dom_key
+    vprobe = valu_probe_summary()
     if strategy == "brute-force":
-        kname = f"k_quant_bf<float, {B}, 0, 1>"
-        work = BF_CANDIDATES * BF_INSTR_PER_EVAL * dom_elems          # exhaustive-search VALU work per launch
-        achieved = work / (dom_ms * 1e-3) / 1e12
-        roofline = {"bound": "alu", "kernel": kname, "achieved": round(achieved, 2),
-                    "peak": round(VALU_PEAK_TOPS, 1), "unit": "T VALU instr/s",
-                    "frac": round(achieved / VALU_PEAK_TOPS, 4),
-                    "work_per_launch": f"{BF_CANDIDATES} candidates x {BF_INSTR_PER_EVAL} VALU instructions x "
-                                       f"{dom_elems} elements (the exhaustive search; the exact branch and bound "
-                                       "evaluates a fraction of the candidates, so frac > 1 is pruning)",
-                    "avg_launch_ms": round(dom_ms, 4)}
-        prof = dominant_profile(kname)
-        if prof and "SQ_INSTS_VALU" in prof:
-            executed = prof["SQ_INSTS_VALU"]["mean"] * 64            # lane-instructions actually issued
-            roofline["executed_valu_instr_per_launch"] = round(executed)
-            roofline["executed_valu_frac"] = round(executed / (dom_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4)
+        roofline = bf_roofline(calls, per_call, dom, B, vprobe)
     else:
-        kname = f"k_quant<float, {B}" if B else dom[0][0].kind
+        dom_ms = float(np.mean([ms for _, ms in dom]))
         nbytes = dom[0][0].nbytes
         achieved = nbytes / (dom_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_launch_ms": round(dom_ms, 4)}
-    traffic = counter_traffic(kname)
-    roofline["traffic"] = None if traffic is None else round(traffic / 1e6, 2)
-    roofline["traffic_unit"] = "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    roofline["algorithmic_MB_per_launch"] = round(dom[0][0].nbytes / 1e6, 2)
-    # the practical HBM ceiling of this access pattern: device copies of the same
-    # four 64 MiB inputs, in the same rotation, into four 64 MiB buffers
-    names = list(X)
-    dsts = [torch.empty_like(X[n]) for n in names]
-    copy_ms = []
-    for i in range(32 + 4):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dsts[(i + 1) % 4].copy_(X[names[i % 4]])
-        e1.record()
-        copy_ms.append((e0, e1))
-    torch.cuda.synchronize()
-    cms = float(np.mean([a.elapsed_time(b) for a, b in copy_ms[4:]]))
-    copy_gbs = 2 * X[names[0]].numel() * 4 / (cms * 1e6)
-    del dsts
-    for k, v in breakdown.items():
-        v["frac_of_copy"] = round(v["GB/s"] / copy_gbs, 4)
+        roofline = {"bound": "hbm", "kernel": f"k_quant<float, {B}" if B else dom[0][0].kind,
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_launch_ms": round(dom_ms, 4), "traffic": None}
+
+    del flush
+    print("[bench] probes (HBM stream ceilings, VALU rates)", file=sys.stderr, flush=True)
+    probes = run_probes(torch, dev, reps=5)
+    rot = probes["hbm"]["copy (streaming stores), four 64 MiB tensors in rotation, warm"]["GB/s"]
+    for v in breakdown.values():
+        v["frac_of_copy"] = round(v["GB/s"] / rot, 4)
+
+    configs = None
+    if not args.no_configs:
+        print("[bench] per-config lines (C1, C3, C4, C5)", file=sys.stderr, flush=True)
+        cfgs, cbld = build_configs(F, S, torch, dev)
+        flush = Flusher(torch, dev)
+        configs = time_configs(torch, cfgs, flush)
+        del cfgs, cbld, flush
+        torch.cuda.empty_cache()
     if args.no_extras:
         search = ue5m3 = hist = gemm = {"what": "not measured (--no-extras)"}
     else:
+        print("[bench] widenings (scale search, UE5M3, histogram, GEMM)", file=sys.stderr, flush=True)
         search = time_quantize_configs(F, torch, X["normal"], [
             ("absmax", F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_SEARCH)),
             ("4-over-6", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_SEARCH)),
@@ -672,6 +1087,7 @@ def main():
     stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
     sb = sum(c.nbytes for c, _ in stream_quant)
     sms = sum(ms for _, ms in stream_quant)
+    scms = sum(cold_ms[id(c)] for c, _ in stream_quant)
 
     result = {
         "metric": "FP4 quantize+dequant GB/s and Gelem/s per strategy; % of HBM/VALU peak",
@@ -694,8 +1110,18 @@ def main():
         "roofline": roofline,
         "streaming_absmax_4over6": {"GB/s": round(sb / (sms * 1e6), 1),
                                     "hbm_frac": round(sb / (sms * 1e6) / HBM_PEAK_GBS, 4),
-                                    "frac_of_copy": round(sb / (sms * 1e6) / copy_gbs, 4)},
+                                    "GB/s_cold": round(sb / (scms * 1e6), 1),
+                                    "hbm_frac_cold": round(sb / (scms * 1e6) / HBM_PEAK_GBS, 4),
+                                    "frac_of_copy": round(sb / (sms * 1e6) / rot, 4)},
+        "cold_step": {"GB/s": round(step_bytes / (sum(cold_ms.values()) * 1e6), 1),
+                      "what": "the step's calls each timed once after a cache flush (1 GiB read on the same "
+                              "stream, outside the events); GB/s of the step's algorithmic bytes over the sum of "
+                              "the call times"},
         "per_strategy": breakdown,
+        "configs": configs,
+        "hbm_reference": dict(probes["hbm"], what="hand-written stream kernels (libfp4q_probe.so): 16-byte "
+                                                  "accesses, best over 4-32 workgroups per CU; cold = after a "
+                                                  "1 GiB read"),
         "global_scale_search": dict({"what": "not part of the step: NVFP4 block 16 quantize of the 4096x4096 "
                                              "N(0,1) input with the per-tensor scale searched over 32 "
                                              "candidates (abs-max pre-pass, 32-candidate scoring, tree "
@@ -705,24 +1131,18 @@ def main():
                                       "UE5M3 block scales (no per-tensor scale), every output"}, **ue5m3),
         "code_histogram": hist,
         "mxfp4_gemm": gemm,
-        "copy_reference": {"GB/s": round(copy_gbs, 1), "hbm_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
-                           "what": "device copy (read + write bytes) of the four 64 MiB inputs in rotation, "
-                                   "the same access pattern as the quantize calls; per_strategy frac_of_copy "
-                                   "is GB/s relative to it"},
     }
 
     if not args.no_cpu_baseline:
         from oracle import oracle as O
         O.build()
-        print(f"[bench] oracle on {args.cpu_rows} rows per tensor (1 thread)", file=sys.stderr, flush=True)
-        nb, dt = cpu_baseline(O, S, host, args.cpu_rows)
-        result["cpu_baseline"] = {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                                  "sample": f"the step's call list on the first {args.cpu_rows} rows of each "
-                                            f"4096x4096 tensor ({nb / 1e6:.1f} MB algorithmic, {dt:.1f} s)"}
+        print(f"[bench] oracle on {args.cpu_rows} rows per tensor (1 thread, then all cores)", file=sys.stderr,
+              flush=True)
+        result["cpu_baseline"] = cpu_baseline(O, S, host, args.cpu_rows)
     if args.calls_out:
         with open(args.calls_out, "w") as f:
-            json.dump([{"name": c.name, "tensor": c.meta.get("tensor"), "ms": ms, "bytes": c.nbytes}
-                       for c, ms in per_call], f, indent=0)
+            json.dump([{"name": c.name, "tensor": c.meta.get("tensor"), "ms": ms, "ms_cold": cold_ms[id(c)],
+                        "bytes": c.nbytes} for c, ms in per_call], f, indent=0)
     line = json.dumps(result)
     print(line, flush=True)
     if args.json_out:

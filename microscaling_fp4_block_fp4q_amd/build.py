@@ -4,6 +4,8 @@
 
 Each csrc/*.hip translation unit is compiled by its own hipcc process (in
 parallel), then linked into microscaling_fp4_block_fp4q_amd/libfp4q.so.
+The measurement probes of the benchmark (probe/*.hip: HBM streams and VALU
+issue rates, not part of the path) become libfp4q_probe.so.
 
 Floating-point flags are part of the numerical contract: no FMA
 contraction, correctly rounded fp32 division, fp32 denormals kept, no
@@ -23,6 +25,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp4q.so")
+PROBE = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libfp4q_probe.so")
 
 ARCH = os.environ.get("FP4Q_OFFLOAD_ARCH", "gfx950")
 
@@ -50,12 +54,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-def sources() -> list[str]:
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder: str = CSRC) -> list[str]:
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    prefix = "probe_" if os.path.dirname(src) == PROBE else ""
+    obj = os.path.join(BUILD, prefix + os.path.basename(src)[:-4] + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -63,21 +68,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every translation unit and link libfp4q.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every translation unit, link libfp4q.so and the benchmark's
+    probe library; returns the path of libfp4q.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    probe_srcs = sources(PROBE)
+    jobs = jobs or min(len(srcs) + len(probe_srcs), max(1, (os.cpu_count() or 4)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -10,6 +10,7 @@ names (``quantize`` ...) also allocate the outputs with torch.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -153,6 +154,54 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Make the launch stream current while outputs and workspace are
+    allocated, so that the caching allocator orders their reuse after the
+    launches on that stream."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _dense(t, dtype, shape, what):
+    """A buffer the C ABI addresses as dense memory: device tensor of the
+    given element type and shape, contiguous (None passes)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{what}: expected a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous tensor")
+
+
+def _scalar_g(g, what="g"):
+    if g is None:
+        return
+    if not isinstance(g, torch.Tensor) or g.device.type != "cuda" or g.dtype != torch.float32 or g.numel() < 1:
+        raise ValueError(f"{what}: expected a device float32 tensor of at least one element")
+
+
+def _workspace_ok(ws, cfg, rows, cols):
+    need = workspace_bytes(cfg, rows, cols)
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace: expected a contiguous device tensor")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace: {need} bytes needed, {ws.numel() * ws.element_size()} given")
+
+
+def _out_2d(t, rows, cols, what):
+    """A [rows, cols] row-strided output or input (unit column stride)."""
+    r, c, ld = _rows_cols_ld(t)
+    if (r, c) != (rows, cols):
+        raise ValueError(f"{what}: expected shape {(rows, cols)}, got {(r, c)}")
+    dtype_code(t)
+    return ld
+
+
 def _check(status: int, what: str):
     if status != OK:
         raise Fp4qError(status, what)
@@ -164,9 +213,15 @@ def _check(status: int, what: str):
 
 def fp4q_quantize(cfg, x, codes, scales, g=None, dequant=None, block_mse=None, workspace=None, stream=None):
     rows, cols, ld = _rows_cols_ld(x)
+    nb = cols // cfg.block
+    _dense(codes, torch.uint8, (rows, cols // 2), "codes")
+    _dense(scales, torch.uint8, (rows, nb), "scales")
+    _dense(block_mse, torch.float32, (rows, nb), "block_mse")
+    _scalar_g(g)
+    _workspace_ok(workspace, cfg, rows, cols)
     dq_dt, ld_dq = F32, cols
     if dequant is not None:
-        _, _, ld_dq = _rows_cols_ld(dequant)
+        ld_dq = _out_2d(dequant, rows, cols, "dequant")
         dq_dt = dtype_code(dequant)
     st = lib().fp4q_quantize(ctypes.byref(cfg), _ptr(x), dtype_code(x), rows, cols, ld, _ptr(codes),
                              _ptr(scales), _ptr(g), _ptr(dequant), dq_dt, ld_dq, _ptr(block_mse),
@@ -176,6 +231,11 @@ def fp4q_quantize(cfg, x, codes, scales, g=None, dequant=None, block_mse=None, w
 
 def fp4q_scale_search(cfg, x, scales, g=None, best_sse=None, workspace=None, stream=None):
     rows, cols, ld = _rows_cols_ld(x)
+    nb = cols // cfg.block
+    _dense(scales, torch.uint8, (rows, nb), "scales")
+    _dense(best_sse, torch.float32, (rows, nb), "best_sse")
+    _scalar_g(g)
+    _workspace_ok(workspace, cfg, rows, cols)
     st = lib().fp4q_scale_search(ctypes.byref(cfg), _ptr(x), dtype_code(x), rows, cols, ld, _ptr(scales),
                                  _ptr(g), _ptr(best_sse), _ptr(workspace), _stream(stream))
     _check(st, "fp4q_scale_search")
@@ -183,6 +243,9 @@ def fp4q_scale_search(cfg, x, scales, g=None, best_sse=None, workspace=None, str
 
 def fp4q_dequantize(cfg, codes, scales, out, g=None, stream=None):
     rows, cols, ld = _rows_cols_ld(out)
+    _dense(codes, torch.uint8, (rows, cols // 2), "codes")
+    _dense(scales, torch.uint8, (rows, cols // cfg.block), "scales")
+    _scalar_g(g)
     st = lib().fp4q_dequantize(ctypes.byref(cfg), _ptr(codes), _ptr(scales), _ptr(g), rows, cols, _ptr(out),
                                dtype_code(out), ld, _stream(stream))
     _check(st, "fp4q_dequantize")
@@ -190,6 +253,11 @@ def fp4q_dequantize(cfg, codes, scales, out, g=None, stream=None):
 
 def fp4q_block_mse(cfg, x, codes, scales, block_mse, g=None, stream=None):
     rows, cols, ld = _rows_cols_ld(x)
+    nb = cols // cfg.block
+    _dense(codes, torch.uint8, (rows, cols // 2), "codes")
+    _dense(scales, torch.uint8, (rows, nb), "scales")
+    _dense(block_mse, torch.float32, (rows, nb), "block_mse")
+    _scalar_g(g)
     st = lib().fp4q_block_mse(ctypes.byref(cfg), _ptr(x), dtype_code(x), rows, cols, ld, _ptr(codes),
                               _ptr(scales), _ptr(g), _ptr(block_mse), _stream(stream))
     _check(st, "fp4q_block_mse")
@@ -197,7 +265,11 @@ def fp4q_block_mse(cfg, x, codes, scales, block_mse, g=None, stream=None):
 
 def fp4q_relaxed_fakequant_fwd(cfg, w, scales, c, sub_block, w_hat, g=None, codes=None, stream=None):
     rows, cols, ld = _rows_cols_ld(w)
-    _, _, ld_out = _rows_cols_ld(w_hat)
+    _dense(scales, torch.uint8, (rows, cols // cfg.block), "scales")
+    _dense(c, torch.float16, (rows, cols // sub_block), "c")
+    _dense(codes, torch.uint8, (rows, cols // 2), "codes")
+    _scalar_g(g)
+    ld_out = _out_2d(w_hat, rows, cols, "w_hat")
     st = lib().fp4q_relaxed_fakequant_fwd(ctypes.byref(cfg), _ptr(w), dtype_code(w), rows, cols, ld,
                                           _ptr(scales), _ptr(g), _ptr(c), sub_block, _ptr(w_hat),
                                           dtype_code(w_hat), ld_out, _ptr(codes), _stream(stream))
@@ -206,7 +278,11 @@ def fp4q_relaxed_fakequant_fwd(cfg, w, scales, c, sub_block, w_hat, g=None, code
 
 def fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g=None, stream=None):
     rows, cols, ld = _rows_cols_ld(w)
-    _, _, ld_g = _rows_cols_ld(grad_out)
+    _dense(scales, torch.uint8, (rows, cols // cfg.block), "scales")
+    _dense(c, torch.float16, (rows, cols // sub_block), "c")
+    _dense(grad_c, torch.float32, (rows, cols // sub_block), "grad_c")
+    _scalar_g(g)
+    ld_g = _out_2d(grad_out, rows, cols, "grad_out")
     st = lib().fp4q_relaxed_fakequant_bwd(ctypes.byref(cfg), _ptr(w), dtype_code(w), rows, cols, ld,
                                           _ptr(scales), _ptr(g), _ptr(c), sub_block, _ptr(grad_out),
                                           dtype_code(grad_out), ld_g, _ptr(grad_c), _stream(stream))
@@ -214,7 +290,11 @@ def fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g
 
 
 def fp4q_code_histogram(codes, counts, stream=None):
+    if codes.dim() != 2:
+        raise ValueError("codes: expected a 2-D tensor [rows, cols/2]")
     rows, half = codes.shape
+    _dense(codes, torch.uint8, (rows, half), "codes")
+    _dense(counts, torch.int64, (16,), "counts")
     st = lib().fp4q_code_histogram(_ptr(codes), rows, 2 * half, _ptr(counts), _stream(stream))
     _check(st, "fp4q_code_histogram")
 
@@ -224,10 +304,20 @@ def mxfp4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 
 
 def fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, workspace, stream=None):
+    if a_codes.dim() != 2 or b_codes.dim() != 2:
+        raise ValueError("codes: expected 2-D tensors [rows, K/2]")
     M, N = a_codes.shape[0], b_codes.shape[0]
     K = 2 * a_codes.shape[1]
+    _dense(a_codes, torch.uint8, (M, K // 2), "a_codes")
+    _dense(b_codes, torch.uint8, (N, K // 2), "b_codes")
+    _dense(a_scales, torch.uint8, (M, K // 32), "a_scales")
+    _dense(b_scales, torch.uint8, (N, K // 32), "b_scales")
+    ldc = _out_2d(c, M, N, "c")
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous() \
+            or workspace.numel() * workspace.element_size() < mxfp4_gemm_workspace_bytes(M, N, K):
+        raise ValueError("workspace: expected a contiguous device tensor of mxfp4_gemm_workspace_bytes(M, N, K)")
     st = lib().fp4q_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K, _ptr(c),
-                               dtype_code(c), c.stride(0), _ptr(workspace), _stream(stream))
+                               dtype_code(c), ldc, _ptr(workspace), _stream(stream))
     _check(st, "fp4q_mxfp4_gemm")
 
 
@@ -241,62 +331,70 @@ def _workspace(cfg, rows, cols, device):
 
 
 def quantize(x, cfg, dequant_dtype=None, want_mse=True, scales=None, stream=None):
-    """Quantize a 2-D device tensor; returns dict(codes, scales, g, dequant, mse)."""
+    """Quantize a 2-D device tensor; returns dict(codes, scales, g, dequant, mse).
+    With stream, the outputs are allocated on and the kernels run on it."""
     rows, cols, _ = _rows_cols_ld(x)
     dev = x.device
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-    if scales is None:
-        scales = torch.empty((rows, cols // cfg.block), dtype=torch.uint8, device=dev)
-    g = torch.empty(1, dtype=torch.float32, device=dev)
-    dq = None if dequant_dtype is None else torch.empty((rows, cols), dtype=dequant_dtype, device=dev)
-    mse = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=dev) if want_mse else None
-    fp4q_quantize(cfg, x, codes, scales, g, dq, mse, _workspace(cfg, rows, cols, dev), stream)
+    with _on(stream):
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        if scales is None:
+            scales = torch.empty((rows, cols // cfg.block), dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+        dq = None if dequant_dtype is None else torch.empty((rows, cols), dtype=dequant_dtype, device=dev)
+        mse = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=dev) if want_mse else None
+        fp4q_quantize(cfg, x, codes, scales, g, dq, mse, _workspace(cfg, rows, cols, dev), stream)
     return dict(codes=codes, scales=scales, g=g, dequant=dq, mse=mse)
 
 
 def scale_search(x, cfg, want_sse=True, stream=None):
     rows, cols, _ = _rows_cols_ld(x)
     dev = x.device
-    scales = torch.empty((rows, cols // cfg.block), dtype=torch.uint8, device=dev)
-    g = torch.empty(1, dtype=torch.float32, device=dev)
-    sse = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=dev) if want_sse else None
-    fp4q_scale_search(cfg, x, scales, g, sse, _workspace(cfg, rows, cols, dev), stream)
+    with _on(stream):
+        scales = torch.empty((rows, cols // cfg.block), dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+        sse = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=dev) if want_sse else None
+        fp4q_scale_search(cfg, x, scales, g, sse, _workspace(cfg, rows, cols, dev), stream)
     return dict(scales=scales, g=g, sse=sse)
 
 
 def dequantize(codes, scales, cfg, g=None, out_dtype=torch.float32, stream=None):
     rows, cols = codes.shape[0], codes.shape[1] * 2
-    out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
-    fp4q_dequantize(cfg, codes, scales, out, g, stream)
+    with _on(stream):
+        out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+        fp4q_dequantize(cfg, codes, scales, out, g, stream)
     return out
 
 
 def block_mse(x, codes, scales, cfg, g=None, stream=None):
     rows, cols, _ = _rows_cols_ld(x)
-    out = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=x.device)
-    fp4q_block_mse(cfg, x, codes, scales, out, g, stream)
+    with _on(stream):
+        out = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=x.device)
+        fp4q_block_mse(cfg, x, codes, scales, out, g, stream)
     return out
 
 
 def relaxed_fakequant_fwd(w, scales, c, cfg, sub_block=8, g=None, out_dtype=None, want_codes=False, stream=None):
     rows, cols, _ = _rows_cols_ld(w)
-    w_hat = torch.empty((rows, cols), dtype=out_dtype or w.dtype, device=w.device)
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device) if want_codes else None
-    fp4q_relaxed_fakequant_fwd(cfg, w, scales, c, sub_block, w_hat, g, codes, stream)
+    with _on(stream):
+        w_hat = torch.empty((rows, cols), dtype=out_dtype or w.dtype, device=w.device)
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device) if want_codes else None
+        fp4q_relaxed_fakequant_fwd(cfg, w, scales, c, sub_block, w_hat, g, codes, stream)
     return w_hat, codes
 
 
 def relaxed_fakequant_bwd(w, scales, c, grad_out, cfg, sub_block=8, g=None, stream=None):
     rows, cols, _ = _rows_cols_ld(w)
-    grad_c = torch.empty((rows, cols // sub_block), dtype=torch.float32, device=w.device)
-    fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g, stream)
+    with _on(stream):
+        grad_c = torch.empty((rows, cols // sub_block), dtype=torch.float32, device=w.device)
+        fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g, stream)
     return grad_c
 
 
 def code_histogram(codes, stream=None):
     """Counts of the 16 nibble codes in packed codes [rows, cols/2] (int64 tensor of 16)."""
-    counts = torch.zeros(16, dtype=torch.int64, device=codes.device)
-    fp4q_code_histogram(codes, counts, stream)
+    with _on(stream):
+        counts = torch.zeros(16, dtype=torch.int64, device=codes.device)
+        fp4q_code_histogram(codes, counts, stream)
     return counts
 
 
@@ -313,8 +411,9 @@ def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.float32, wo
     M, N, K = a_codes.shape[0], b_codes.shape[0], 2 * a_codes.shape[1]
     per16 = 16 // torch.empty(0, dtype=out_dtype).element_size()
     ldc = (N + per16 - 1) // per16 * per16
-    c = torch.empty((M, ldc), dtype=out_dtype, device=a_codes.device)[:, :N]
-    if workspace is None:
-        workspace = gemm_workspace(M, N, K, a_codes.device)
-    fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, workspace, stream)
+    with _on(stream):
+        c = torch.empty((M, ldc), dtype=out_dtype, device=a_codes.device)[:, :N]
+        if workspace is None:
+            workspace = gemm_workspace(M, N, K, a_codes.device)
+        fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, workspace, stream)
     return c

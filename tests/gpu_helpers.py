@@ -69,3 +69,41 @@ def sample_rows(n_rows: int, seed: int = 0, k: int = 6) -> np.ndarray:
     rng = np.random.default_rng(seed)
     pick = {0, 1, n_rows // 2, n_rows - 1} | set(rng.choice(n_rows, size=min(k, n_rows), replace=False).tolist())
     return np.array(sorted(pick))
+
+
+def host_threads() -> int:
+    """Threads for the oracle on the host: this process's CPUs, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_rows(fn, arrays, chunk=64, **kw):
+    """Run an oracle entry point over row chunks of the given arrays on the
+    host's cores (ctypes releases the GIL) and stack the results by rows.
+    fn(*row_slices, **kw) returns an array, a tuple of arrays or a dict of
+    arrays with a leading row axis (scalars and None pass through from the
+    first chunk).  Every row of the result is the oracle's own; rows are
+    independent in every entry point called this way (a per-tensor scale is
+    passed in as the user scale)."""
+    import concurrent.futures as cf
+    rows = arrays[0].shape[0]
+    starts = list(range(0, rows, chunk))
+
+    def run(r0):
+        return fn(*(np.ascontiguousarray(a[r0:r0 + chunk]) for a in arrays), **kw)
+
+    with cf.ThreadPoolExecutor(host_threads()) as ex:
+        parts = list(ex.map(run, starts))
+
+    def stack(vals):
+        v0 = vals[0]
+        if isinstance(v0, np.ndarray) and v0.ndim >= 1:
+            return np.concatenate(vals, axis=0)
+        return v0
+
+    first = parts[0]
+    if isinstance(first, dict):
+        return {k: stack([p[k] for p in parts]) for k in first}
+    if isinstance(first, tuple):
+        return tuple(stack([p[i] for p in parts]) for i in range(len(first)))
+    return stack(parts)

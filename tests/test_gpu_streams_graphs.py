@@ -127,3 +127,27 @@ def test_graph_replay_matches_eager(O_lib):
             if name != "counts":
                 assert_same(got[name], want[name], f"replay {k}: {name}")
         counts_sum = check_against_oracle(x, got, counts_sum)
+
+
+def test_allocating_wrappers_take_the_stream_argument(O_lib):
+    """quantize(..., stream=s) with s not the current stream: outputs and
+    workspace are allocated on s and the kernels run on s, while the current
+    stream keeps allocating and filling buffers of the workspace's size (which
+    would reuse a workspace released to the wrong stream)."""
+    x = S.laplace(ROWS, COLS, 61)
+    xt = S.to_torch(x, S.F32, DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    note("allocating wrappers on a stream argument")
+    nbytes = max(F.workspace_bytes(CFG_AMAX, ROWS, COLS), 16)
+    results, junk = [], []
+    for _ in range(6):
+        results.append(F.quantize(xt, CFG_AMAX, dequant_dtype=torch.float32, stream=s))
+        junk.append(torch.full((nbytes,), 255, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    ref = O.quantize(x, fmt=CFG_AMAX.scale_fmt, block=16, strategy=F.FOUR_OVER_SIX,
+                     global_mode=F.GLOBAL_TENSOR_AMAX)
+    for r in results:
+        assert S.from_torch(r["g"])[0].view(np.uint32) == np.float32(ref["g"]).view(np.uint32)
+        for k in ("codes", "scales", "dequant", "mse"):
+            assert_same(S.from_torch(r[k]), ref[k], k)
