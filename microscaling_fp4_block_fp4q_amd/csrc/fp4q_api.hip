@@ -130,7 +130,7 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
     if (tamax) FP4Q_TRY(check_buffer(workspace));
 
     if (tamax) {
-        const int U = unit_of(x_dt, 1, H);
+        const int U = 16 / elem_size(x_dt);       // the pre-pass walks 16-byte chunks
         AmaxArgs aa{};
         aa.x = x;
         aa.ld_x = ld_x;
@@ -141,8 +141,8 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
         FP4Q_TRY(device_status(launch_amax(aa, x_dt, H, kAmaxBlocks, s)));
     }
 
-    const int U = unit_of(x_dt, B, H);
     if (search) {
+        const int U = unit_of(x_dt, B, H);
         GSearchArgs ga{};
         ga.x = x;
         ga.ld_x = ld_x;
@@ -181,6 +181,9 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
         FP4Q_TRY(device_status(launch_gsearch_pick(src, stride, ga.amax_partials, kAmaxBlocks, g_dev, s)));
     }
 
+    // brute force works in units of unit_of() values, the streaming kernel in
+    // 16-byte chunks
+    const int U = cfg->strategy == FP4Q_BRUTE_FORCE ? unit_of(x_dt, B, H) : 16 / elem_size(x_dt);
     QuantArgs qa{};
     qa.x = x;
     qa.ld_x = ld_x;
@@ -277,7 +280,8 @@ fp4q_status fp4q_dequantize(const fp4q_config* cfg, const uint8_t* codes, const 
     FP4Q_TRY(check_buffer(codes));
     FP4Q_TRY(check_buffer(scales));
     FP4Q_TRY(check_tensor(out, out_dt, rows, cols, ld_out));
-    const int DU = cols % 8 == 0 ? 8 : 4;     // output values per lane
+    const int oes = elem_size(out_dt);
+    const int DU = 16 / oes;                  // output values per 16-byte chunk
     DequantArgs a{};
     a.codes = codes;
     a.scales = scales;
@@ -289,7 +293,7 @@ fp4q_status fp4q_dequantize(const fp4q_config* cfg, const uint8_t* codes, const 
     a.out = out;
     a.ld_out = ld_out;
     a.out_dt = out_dt;
-    return device_status(launch_dequant(a, B, DU, grid_for(a.units), (hipStream_t)stream));
+    return device_status(launch_dequant(a, B, oes, grid_for(a.units), (hipStream_t)stream));
 }
 
 fp4q_status fp4q_block_mse(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,
@@ -304,7 +308,7 @@ fp4q_status fp4q_block_mse(const fp4q_config* cfg, const void* x, int x_dt, int6
     FP4Q_TRY(check_buffer(codes));
     FP4Q_TRY(check_buffer(scales));
     FP4Q_TRY(check_buffer(block_mse));
-    const int U = unit_of(x_dt, B, H);
+    const int U = 16 / elem_size(x_dt);       // 16-byte chunks of x
     MseArgs a{};
     a.x = x;
     a.ld_x = ld_x;
@@ -345,7 +349,7 @@ fp4q_status fp4q_relaxed_fakequant_fwd(const fp4q_config* cfg, const void* w, in
     if (rows == 0 || cols == 0) return dtype_ok(out_dt) ? FP4Q_OK : FP4Q_ERR_INVALID_ARG;
     FP4Q_TRY(check_tensor(w_hat, out_dt, rows, cols, ld_out));
     if (codes) FP4Q_TRY(check_buffer(codes));
-    const int U = unit_of(w_dt, cfg->block, 0);
+    const int U = 16 / elem_size(w_dt);       // 16-byte chunks of W
     RelaxedArgs a{};
     a.w = w;
     a.ld_w = ld_w;
@@ -373,7 +377,7 @@ fp4q_status fp4q_relaxed_fakequant_bwd(const fp4q_config* cfg, const void* w, in
     if (rows == 0 || cols == 0) return dtype_ok(g_dt) ? FP4Q_OK : FP4Q_ERR_INVALID_ARG;
     FP4Q_TRY(check_tensor(grad_out, g_dt, rows, cols, ld_g));
     FP4Q_TRY(check_buffer(grad_c));
-    const int U = unit_of(w_dt, cfg->block, 0);
+    const int U = 16 / elem_size(w_dt);       // 16-byte chunks of W
     RelaxedArgs a{};
     a.w = w;
     a.ld_w = ld_w;

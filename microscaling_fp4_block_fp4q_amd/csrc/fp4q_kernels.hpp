@@ -702,114 +702,6 @@ __device__ __forceinline__ DqSink<U> dq_sink(const P& p, char* lds, int lane, in
 // Kernels
 // ---------------------------------------------------------------------------
 
-// Partial per-tensor abs-max (of the rotated values when H != 0) for
-// hierarchical scaling.  One result per workgroup in p.partials.
-template <class InT, int H>
-__global__ __launch_bounds__(kThreads) void k_amax(AmaxArgs p) {
-    constexpr int U = unit_elems<InT, 1, H>();
-    constexpr int UNROLL = 4;
-    const InT* x = reinterpret_cast<const InT*>(p.x);
-    uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t u0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; u0 < p.units; u0 += stride * UNROLL) {
-        float y[UNROLL][U];
-#pragma unroll
-        for (int k = 0; k < UNROLL; ++k) {
-            const int64_t u = u0 + k * stride;
-            if (u < p.units) {
-                load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, p.contiguous), y[k]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < U; ++i) y[k][i] = 0.0f;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < UNROLL; ++k) {
-            if constexpr (H > 0) fwht_segments<H, U>(y[k]);
-#pragma unroll
-            for (int i = 0; i < U; ++i) m = max(m, as_u(y[k][i]) & 0x7FFFFFFFu);
-        }
-    }
-    m = workgroup_max_u32(m);
-    if (threadIdx.x == 0) p.partials[blockIdx.x] = m;
-}
-
-// Quantize: scale selection, encode, pack, dequantize, block error.
-// Each wave walks tiles of 64 units; lane l of a tile owns unit 64 t + l.
-template <class InT, int B, int H, int SF, int ST>
-__global__ __launch_bounds__(kThreads) void k_quant(QuantArgs p) {
-    constexpr int U = unit_elems<InT, B, H>();
-    constexpr int NB = U / B;
-    constexpr int WAVE_LDS = kTileUnits * slot_bytes<U>();
-    __shared__ __attribute__((aligned(16))) char s_tiles[kThreads / 64][WAVE_LDS];
-    static_assert(ST != ST_BRUTE_FORCE, "brute force runs in k_quant_bf");
-
-    const InT* x = reinterpret_cast<const InT*>(p.x);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    char* lds = s_tiles[wave];
-
-    const float g = workgroup_global_scale(p);
-    if (blockIdx.x == 0 && threadIdx.x == 0 && p.g_out) *p.g_out = g;
-    const float six_g = 6.0f * g, four_g = 4.0f * g;
-
-    const int64_t ntiles = (p.units + kTileUnits - 1) / kTileUnits;
-    const int64_t tstride = (int64_t)gridDim.x * (kThreads / 64);
-    // Units of 16 or more values: each lane loads its own unit of the next
-    // tile while this one is quantized (one tile of loads in flight per wave
-    // during the compute; measured 2-21 % faster for B = 16, 32 and the
-    // rotations).  Smaller units load through the LDS slots, coalesced,
-    // without prefetch (prefetching them measured 0-5 % slower).
-    constexpr bool PREFETCH = U >= 16;
-    float ynext[U];                       // unused without PREFETCH
-    auto fetch = [&](int64_t tt) {
-        const int64_t uu = tt * kTileUnits + lane;
-        if (tt < ntiles && uu < p.units) {
-            load_elems<InT, U>(x + unit_offset<U>(uu, p.units_per_row, p.ld_x, p.contiguous), ynext);
-        } else {
-#pragma unroll
-            for (int i = 0; i < U; ++i) ynext[i] = 0.0f;
-        }
-    };
-    if constexpr (PREFETCH) fetch((int64_t)blockIdx.x * (kThreads / 64) + wave);
-    for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < ntiles; t += tstride) {
-        const int64_t u0 = t * kTileUnits;
-        const int nvalid = (int)min<int64_t>(kTileUnits, p.units - u0);
-        const int64_t u = u0 + lane;
-        const bool active = lane < nvalid;
-
-        float y[U];
-        if constexpr (PREFETCH) {
-#pragma unroll
-            for (int i = 0; i < U; ++i) y[i] = ynext[i];
-            fetch(t + tstride);
-        } else if (p.contiguous) {
-            tile_load<InT, U>(x + u0 * U, nvalid, lds, lane, y);
-        } else if (active) {
-            load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, false), y);
-        } else {
-#pragma unroll
-            for (int i = 0; i < U; ++i) y[i] = 0.0f;
-        }
-        if constexpr (H > 0) fwht_segments<H, U>(y);
-
-        uint32_t given[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) given[b] = (ST == ST_GIVEN && active) ? p.scales[u * NB + b] : 0u;
-
-        uint32_t cw[code_words(U)];
-#pragma unroll
-        for (int i = 0; i < code_words(U); ++i) cw[i] = 0;
-        const DqSink<U> sink = dq_sink<U>(p, lds, lane, u, active);
-        uint32_t sc[NB];
-        float sse[NB];
-        static_for<NB>([&](auto bi) {
-            constexpr int b = decltype(bi)::value;
-            quant_block<SF, ST, B, b>(y, g, six_g, four_g, p.prevent_zero, given[b], cw, sink, sc[b], sse[b]);
-        });
-        store_unit_outputs<B, U>(p, u0, nvalid, lane, lds, cw, sc, sse, ST != ST_GIVEN);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Per-tensor scale search (MR-GPTQ page, section 2.2: scales chosen per
 // tensor for minimum MSE).  Candidate g_j = fl(g0 (1 - j/64)); its score is
@@ -1278,171 +1170,6 @@ __device__ __forceinline__ float stored_scale(int fmt, uint32_t code, float g, b
     const float S = ue5m3_value(code) * g;
     usable = code != kUE5M3NaN && scale_usable(S);
     return S;
-}
-
-// Dequantize codes + scales.  One lane per DU consecutive output values
-// (DU = 8, or 4 when rows are not a multiple of 8 long): consecutive lanes
-// read consecutive code bytes and write consecutive output bytes.
-template <int B, int DU>
-__global__ __launch_bounds__(kThreads) void k_dequant(DequantArgs p) {
-    const float g = read_g(p.g_dev);
-    const int64_t n = p.units;                        // rows * cols / DU
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < n; j += stride) {
-        const int64_t e0 = j * DU;                    // flat element index (codes and scales are dense)
-        uint32_t c[DU];
-        load_codes<DU>(p.codes + e0 / 2, c);
-        constexpr int NBD = DU > B ? DU / B : 1;      // blocks touched by this lane
-        float S[NBD];
-        bool nan_block[NBD];
-#pragma unroll
-        for (int b = 0; b < NBD; ++b) {
-            bool usable;
-            S[b] = stored_scale(p.scale_fmt, p.scales[e0 / B + b], g, usable);
-            nan_block[b] = !usable;
-        }
-        float v[DU];
-#pragma unroll
-        for (int i = 0; i < DU; ++i) {
-            const int b = DU > B ? i / B : 0;
-            const float sgn = as_f((c[i] & 8u) << 28);
-            v[i] = nan_block[b] ? canonical_nan_like(sgn) : with_sign_of(e2m1_value(c[i]) * S[b], sgn);
-        }
-        int64_t off = e0;
-        if (p.ld_out != p.cols) {
-            const int64_t row = e0 / p.cols;
-            off = row * p.ld_out + (e0 - row * p.cols);
-        }
-        store_elems_rt<DU>(p.out, p.out_dt, off, v);
-    }
-}
-
-// Per-block MSE of (rotated) x against stored codes + scales.
-template <class InT, int B, int H>
-__global__ __launch_bounds__(kThreads) void k_block_mse(MseArgs p) {
-    constexpr int U = unit_elems<InT, B, H>();
-    constexpr int NB = U / B;
-    const InT* x = reinterpret_cast<const InT*>(p.x);
-    const float g = read_g(p.g_dev);
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < p.units; u += stride) {
-        float y[U];
-        load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, false), y);
-        if constexpr (H > 0) fwht_segments<H, U>(y);
-        uint32_t c[U];
-        load_codes<U>(p.codes + u * (U / 2), c);
-        float mse[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            bool usable;
-            const float S = stored_scale(p.scale_fmt, p.scales[u * NB + b], g, usable);
-            const bool nan_block = !usable;
-            float e[B];
-#pragma unroll
-            for (int i = 0; i < B; ++i) {
-                const uint32_t q = c[b * B + i];
-                const float yh = with_sign_of(e2m1_value(q) * S, as_f((q & 8u) << 28));
-                const float d = y[b * B + i] - yh;
-                e[i] = d * d;
-            }
-            const float m = tree_sum<B>(e) * (1.0f / (float)B);
-            mse[b] = (nan_block || m != m) ? as_f(kQNaN) : m;
-        }
-        store_stream_f32<NB>(p.mse + u * NB, mse);
-    }
-}
-
-__device__ __forceinline__ float f16_value(uint16_t h) { return f16_bits_to_f32(h); }
-
-// FOCUS relaxed fake-quant forward (FOCUS page, methods 2-3):
-// S_q = fl(S_dq c_k), u = fl(|W| / S_q), What = (-1)^s fl(grid * S_dq).
-template <class InT, int B, int K>
-__global__ __launch_bounds__(kThreads) void k_relaxed_fwd(RelaxedArgs p) {
-    constexpr int U = unit_elems<InT, B, 0>();
-    constexpr int NB = U / B;
-    const InT* w = reinterpret_cast<const InT*>(p.w);
-    const float g = read_g(p.g_dev);
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    const int64_t nk = p.cols / K;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < p.units; u += stride) {
-        const int64_t row = u / p.units_per_row;
-        const int64_t col0 = (u - row * p.units_per_row) * U;
-        float y[U];
-        load_elems<InT, U>(w + row * p.ld_w + col0, y);
-        uint32_t code[U];
-        float wh[U];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            bool ok_dq;
-            const float S_dq = stored_scale(p.scale_fmt, p.scales[u * NB + b], g, ok_dq);
-#pragma unroll
-            for (int k = 0; k < B / K; ++k) {
-                const float c_k = f16_value(p.c[row * nk + (col0 + b * B) / K + k]);
-                const float S_q = S_dq * c_k;
-                const bool ok = ok_dq && scale_usable(S_q);
-                const bool fast = fast_quotient_range(S_q);
-                const float R_q = fast ? 1.0f / S_q : 0.0f;
-#pragma unroll
-                for (int i = 0; i < K; ++i) {
-                    const int j = b * B + k * K + i;
-                    const float a = fabsf(y[j]);
-                    const float u_ = fast ? quotient<SF_E4M3, true>(a, S_q, R_q) : quotient<SF_E4M3, false>(a, S_q, 0.0f);
-                    float rr = e2m1_round(u_);
-                    rr = (a == a) ? rr : 0.0f;
-                    const uint32_t s = (as_u(y[j]) >> 31) << 3;
-                    code[j] = ok ? (s | e2m1_code_of(rr)) : s;
-                    wh[j] = ok ? with_sign_of(rr * S_dq, y[j]) : canonical_nan_like(y[j]);
-                }
-            }
-        }
-        store_elems_rt<U>(p.w_hat, p.out_dt, row * p.ld_out + col0, wh);
-        if (p.codes) store_codes<U>(p.codes + u * (U / 2), code);
-    }
-}
-
-// Straight-through backward to c_k (FOCUS page, method 1):
-// grad_c = fl(-A / fl(c c)), A = tree sum of [S_q > 0, |u| <= 6] fl(G W).
-template <class InT, int B, int K>
-__global__ __launch_bounds__(kThreads) void k_relaxed_bwd(RelaxedArgs p) {
-    constexpr int U = unit_elems<InT, B, 0>();
-    constexpr int NB = U / B;
-    const InT* w = reinterpret_cast<const InT*>(p.w);
-    const float g = read_g(p.g_dev);
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    const int64_t nk = p.cols / K;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < p.units; u += stride) {
-        const int64_t row = u / p.units_per_row;
-        const int64_t col0 = (u - row * p.units_per_row) * U;
-        float y[U], G[U];
-        load_elems<InT, U>(w + row * p.ld_w + col0, y);
-        load_elems_rt<U>(p.grad, p.g_dt, row * p.ld_g + col0, G);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            bool ok_dq;
-            const float S_dq = stored_scale(p.scale_fmt, p.scales[u * NB + b], g, ok_dq);
-#pragma unroll
-            for (int k = 0; k < B / K; ++k) {
-                const int64_t ci = row * nk + (col0 + b * B) / K + k;
-                const float c_k = f16_value(p.c[ci]);
-                const float S_q = S_dq * c_k;
-                const bool ok = ok_dq && scale_usable(S_q);
-                const bool fast = fast_quotient_range(S_q);
-                const float R_q = fast ? 1.0f / S_q : 0.0f;
-                float t[K];
-#pragma unroll
-                for (int i = 0; i < K; ++i) {
-                    const int j = b * B + k * K + i;
-                    const float a = fabsf(y[j]);
-                    const float u_ = fast ? quotient<SF_E4M3, true>(a, S_q, R_q) : quotient<SF_E4M3, false>(a, S_q, 0.0f);
-                    const bool inside = (S_q > 0.0f) && (u_ <= 6.0f);
-                    t[i] = inside ? G[j] * y[j] : 0.0f;
-                }
-                const float A = tree_sum<K>(t);
-                const float out = -A / (c_k * c_k);
-                p.grad_c[ci] = (ok && out == out) ? out : as_f(kQNaN);
-            }
-        }
-    }
 }
 
 }  // namespace fp4q_dev

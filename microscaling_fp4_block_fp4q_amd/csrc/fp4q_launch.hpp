@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fp4q_kernels.hpp"
+#include "fp4q_stream.hpp"
 
 namespace fp4q_dev {
 
@@ -30,7 +31,7 @@ hipError_t launch_code_hist(const uint8_t* codes, int64_t nbytes, unsigned long 
                             hipStream_t s);
 hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t s);
 hipError_t launch_write_g(float* g_dev, float g, hipStream_t s);
-hipError_t launch_dequant(const DequantArgs& a, int B, int DU, int grid, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, int B, int out_es, int grid, hipStream_t s);
 hipError_t launch_block_mse(const MseArgs& a, int x_dt, int B, int H, int grid, hipStream_t s);
 hipError_t launch_relaxed_fwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s);
 hipError_t launch_relaxed_bwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s);
@@ -68,11 +69,20 @@ hipError_t launch_resident(const Args& a, int grid, hipStream_t s) {
 // fp32); larger blocks hold at most five anyway.
 constexpr int kBfMaxWorkgroupsPerCU = 6;
 
-// Template dispatch over block size, rotation size, scale format and strategy.
+// Template dispatch over block size, rotation size, scale format and
+// strategy.  The streaming kernel takes a.units in 16-byte chunks and sizes
+// its grid itself (R chunks per lane per trip, at most the resident
+// workgroups); brute force takes units of unit_elems values.
 template <class InT, int B, int H, int SF, int ST>
 hipError_t launch_quant_t(const QuantArgs& a, int grid, hipStream_t s) {
-    if constexpr (ST == ST_BRUTE_FORCE) return launch_resident<k_quant_bf<InT, B, H, SF>, kBfMaxWorkgroupsPerCU>(a, grid, s);
-    else return launch_resident<k_quant<InT, B, H, SF, ST>>(a, grid, s);
+    if constexpr (ST == ST_BRUTE_FORCE) {
+        return launch_resident<k_quant_bf<InT, B, H, SF>, kBfMaxWorkgroupsPerCU>(a, grid, s);
+    } else {
+        constexpr int R = stream_rounds<InT>();
+        const int64_t per_wg = (int64_t)kThreads * R;
+        const int64_t g = (a.units + per_wg - 1) / per_wg;
+        return launch_resident<k_qstream<InT, B, H, SF, ST, R>>(a, (int)(g < 1 ? 1 : (g > (1 << 20) ? (1 << 20) : g)), s);
+    }
 }
 
 template <class InT, int B, int H, int SF>

@@ -130,12 +130,15 @@ hipError_t launch_code_hist(const uint8_t* codes, int64_t nbytes, unsigned long 
     return hipGetLastError();
 }
 
+// The pre-pass always runs kAmaxBlocks workgroups (one partial each); a.units
+// counts 16-byte chunks.
 template <class InT>
 static hipError_t amax_h(const AmaxArgs& a, int H, int grid, hipStream_t s) {
+    constexpr int R = stream_rounds<InT>();
     switch (H) {
-    case 0: hipLaunchKernelGGL((k_amax<InT, 0>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_amax<InT, 16>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_amax<InT, 32>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((k_amax_stream<InT, 0, R>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_amax_stream<InT, 16, R>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_amax_stream<InT, 32, R>), dim3(grid), dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -150,98 +153,121 @@ hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t
     return hipErrorInvalidValue;
 }
 
-template <int DU>
-static hipError_t dequant_b(const DequantArgs& a, int B, int grid, hipStream_t s) {
+// Grid of a chunk-per-lane kernel: R chunks per lane per trip, at most the
+// resident workgroups (launch_resident caps it).
+template <int R>
+static int stream_grid(int64_t units) {
+    const int64_t per_wg = (int64_t)kThreads * R;
+    const int64_t g = (units + per_wg - 1) / per_wg;
+    return (int)(g < 1 ? 1 : (g > (1 << 20) ? (1 << 20) : g));
+}
+
+constexpr int kDqRounds = 4;
+
+// a.units counts chunks of 16 bytes of output.
+template <int OE>
+static hipError_t dequant_b(const DequantArgs& a, int B, hipStream_t s) {
+    const int grid = stream_grid<kDqRounds>(a.units);
     switch (B) {
-    case 4: return launch_resident<k_dequant<4, DU>>(a, grid, s);
-    case 8: return launch_resident<k_dequant<8, DU>>(a, grid, s);
-    case 16: return launch_resident<k_dequant<16, DU>>(a, grid, s);
-    case 32: return launch_resident<k_dequant<32, DU>>(a, grid, s);
+    case 4: return launch_resident<k_dq_stream<4, OE, kDqRounds>>(a, grid, s);
+    case 8: return launch_resident<k_dq_stream<8, OE, kDqRounds>>(a, grid, s);
+    case 16: return launch_resident<k_dq_stream<16, OE, kDqRounds>>(a, grid, s);
+    case 32: return launch_resident<k_dq_stream<32, OE, kDqRounds>>(a, grid, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_dequant(const DequantArgs& a, int B, int DU, int grid, hipStream_t s) {
-    return DU == 8 ? dequant_b<8>(a, B, grid, s) : dequant_b<4>(a, B, grid, s);
+hipError_t launch_dequant(const DequantArgs& a, int B, int out_es, int grid, hipStream_t s) {
+    (void)grid;
+    return out_es == 4 ? dequant_b<4>(a, B, s) : dequant_b<2>(a, B, s);
 }
 
+// a.units counts 16-byte chunks of x.
 template <class InT, int B>
-static hipError_t mse_h(const MseArgs& a, int H, int grid, hipStream_t s) {
+static hipError_t mse_h(const MseArgs& a, int H, hipStream_t s) {
+    constexpr int R = stream_rounds<InT>();
+    const int grid = stream_grid<R>(a.units);
     switch (H) {
-    case 0: return launch_resident<k_block_mse<InT, B, 0>>(a, grid, s);
-    case 16: return launch_resident<k_block_mse<InT, B, 16>>(a, grid, s);
-    case 32: return launch_resident<k_block_mse<InT, B, 32>>(a, grid, s);
+    case 0: return launch_resident<k_mse_stream<InT, B, 0, R>>(a, grid, s);
+    case 16: return launch_resident<k_mse_stream<InT, B, 16, R>>(a, grid, s);
+    case 32: return launch_resident<k_mse_stream<InT, B, 32, R>>(a, grid, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <class InT>
-static hipError_t mse_b(const MseArgs& a, int B, int H, int grid, hipStream_t s) {
+static hipError_t mse_b(const MseArgs& a, int B, int H, hipStream_t s) {
     switch (B) {
-    case 4: return mse_h<InT, 4>(a, H, grid, s);
-    case 8: return mse_h<InT, 8>(a, H, grid, s);
-    case 16: return mse_h<InT, 16>(a, H, grid, s);
-    case 32: return mse_h<InT, 32>(a, H, grid, s);
+    case 4: return mse_h<InT, 4>(a, H, s);
+    case 8: return mse_h<InT, 8>(a, H, s);
+    case 16: return mse_h<InT, 16>(a, H, s);
+    case 32: return mse_h<InT, 32>(a, H, s);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_block_mse(const MseArgs& a, int x_dt, int B, int H, int grid, hipStream_t s) {
+    (void)grid;
     switch (x_dt) {
-    case DT_F32: return mse_b<float>(a, B, H, grid, s);
-    case DT_BF16: return mse_b<bf16_t>(a, B, H, grid, s);
-    case DT_F16: return mse_b<f16_t>(a, B, H, grid, s);
+    case DT_F32: return mse_b<float>(a, B, H, s);
+    case DT_BF16: return mse_b<bf16_t>(a, B, H, s);
+    case DT_F16: return mse_b<f16_t>(a, B, H, s);
     }
     return hipErrorInvalidValue;
 }
 
+// a.units counts 16-byte chunks of W.
 template <bool BWD, class InT, int B, int K>
-static hipError_t relaxed_launch(const RelaxedArgs& a, int grid, hipStream_t s) {
+static hipError_t relaxed_launch(const RelaxedArgs& a, hipStream_t s) {
     if constexpr (K <= B) {
-        if constexpr (BWD) return launch_resident<k_relaxed_bwd<InT, B, K>>(a, grid, s);
-        else return launch_resident<k_relaxed_fwd<InT, B, K>>(a, grid, s);
+        constexpr int R = stream_rounds<InT>();
+        const int grid = stream_grid<R>(a.units);
+        if constexpr (BWD) return launch_resident<k_relaxed_bwd_stream<InT, B, K, R>>(a, grid, s);
+        else return launch_resident<k_relaxed_fwd_stream<InT, B, K, R>>(a, grid, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <bool BWD, class InT, int B>
-static hipError_t relaxed_k(const RelaxedArgs& a, int K, int grid, hipStream_t s) {
+static hipError_t relaxed_k(const RelaxedArgs& a, int K, hipStream_t s) {
     switch (K) {
-    case 4: return relaxed_launch<BWD, InT, B, 4>(a, grid, s);
-    case 8: return relaxed_launch<BWD, InT, B, 8>(a, grid, s);
-    case 16: return relaxed_launch<BWD, InT, B, 16>(a, grid, s);
-    case 32: return relaxed_launch<BWD, InT, B, 32>(a, grid, s);
+    case 4: return relaxed_launch<BWD, InT, B, 4>(a, s);
+    case 8: return relaxed_launch<BWD, InT, B, 8>(a, s);
+    case 16: return relaxed_launch<BWD, InT, B, 16>(a, s);
+    case 32: return relaxed_launch<BWD, InT, B, 32>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <bool BWD, class InT>
-static hipError_t relaxed_b(const RelaxedArgs& a, int B, int K, int grid, hipStream_t s) {
+static hipError_t relaxed_b(const RelaxedArgs& a, int B, int K, hipStream_t s) {
     switch (B) {
-    case 4: return relaxed_k<BWD, InT, 4>(a, K, grid, s);
-    case 8: return relaxed_k<BWD, InT, 8>(a, K, grid, s);
-    case 16: return relaxed_k<BWD, InT, 16>(a, K, grid, s);
-    case 32: return relaxed_k<BWD, InT, 32>(a, K, grid, s);
+    case 4: return relaxed_k<BWD, InT, 4>(a, K, s);
+    case 8: return relaxed_k<BWD, InT, 8>(a, K, s);
+    case 16: return relaxed_k<BWD, InT, 16>(a, K, s);
+    case 32: return relaxed_k<BWD, InT, 32>(a, K, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <bool BWD>
-static hipError_t relaxed_dt(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s) {
+static hipError_t relaxed_dt(const RelaxedArgs& a, int w_dt, int B, int K, hipStream_t s) {
     switch (w_dt) {
-    case DT_F32: return relaxed_b<BWD, float>(a, B, K, grid, s);
-    case DT_BF16: return relaxed_b<BWD, bf16_t>(a, B, K, grid, s);
-    case DT_F16: return relaxed_b<BWD, f16_t>(a, B, K, grid, s);
+    case DT_F32: return relaxed_b<BWD, float>(a, B, K, s);
+    case DT_BF16: return relaxed_b<BWD, bf16_t>(a, B, K, s);
+    case DT_F16: return relaxed_b<BWD, f16_t>(a, B, K, s);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_relaxed_fwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s) {
-    return relaxed_dt<false>(a, w_dt, B, K, grid, s);
+    (void)grid;
+    return relaxed_dt<false>(a, w_dt, B, K, s);
 }
 
 hipError_t launch_relaxed_bwd(const RelaxedArgs& a, int w_dt, int B, int K, int grid, hipStream_t s) {
-    return relaxed_dt<true>(a, w_dt, B, K, grid, s);
+    (void)grid;
+    return relaxed_dt<true>(a, w_dt, B, K, s);
 }
 
 }  // namespace fp4q_dev

@@ -22,6 +22,15 @@
 //       free quotient at a scale read from LDS, E2M1 rounding, dequantized
 //       product, difference, square, balanced-tree sum over a block of 16).
 //       The executed instruction count comes from the SQ_INSTS_VALU counter.
+//
+//   int fp4q_probe_fp4_convert(unsigned long long* mismatches, void* stream);
+//       Every non-NaN fp32 bit pattern u (2^32 - 2^24 values) through the
+//       gfx950 pair converts fp32 -> FP4 (E2M1, scale 1) and back, against
+//       the round-half-to-even E2M1 rounding with saturation at 6 that the
+//       library computes with ordinary arithmetic: mismatches[0] counts
+//       nibbles (sign and magnitude) that differ, mismatches[1] decoded
+//       values whose bits differ.  mismatches[2] must be zeroed by the caller
+//       (it receives the number of patterns checked).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -162,6 +171,35 @@ __global__ __launch_bounds__(kThreads) void k_valu(int iters, float* out) {
     out[gid] = s;
 }
 
+// Exhaustive check of the hardware FP4 pair convert, 2^32 patterns: each
+// thread takes 64 consecutive patterns (32 pairs).
+__global__ __launch_bounds__(kThreads) void k_fp4_convert(unsigned long long* mismatches) {
+    const uint64_t base = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * 64u;
+    unsigned long long bad_code = 0, bad_value = 0, checked = 0;
+    for (int k = 0; k < 64; k += 2) {
+        const uint32_t b0 = (uint32_t)(base + k), b1 = b0 + 1u;
+        const float u0 = as_f(b0), u1 = as_f(b1);
+        const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, u0, u1, 1.0f, 0);
+        const auto back = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(hw, 1.0f, 0);
+        const float uu[2] = {u0, u1};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float u = uu[e];
+            if (u != u) continue;
+            const float r = e2m1_round(fabsf(u));
+            const uint32_t want = ((as_u(u) >> 31) << 3) | e2m1_code_of(r);
+            const uint32_t got = (hw >> (4 * e)) & 15u;
+            const float want_v = as_f(as_u(r) | (as_u(u) & 0x80000000u));
+            bad_code += got != want;
+            bad_value += as_u(back[e]) != as_u(want_v);
+            ++checked;
+        }
+    }
+    if (bad_code) atomicAdd(&mismatches[0], bad_code);
+    if (bad_value) atomicAdd(&mismatches[1], bad_value);
+    atomicAdd(&mismatches[2], checked);
+}
+
 template <int KIND>
 hipError_t launch_valu(int iters, int grid, float* out, hipStream_t s) {
     hipLaunchKernelGGL(k_valu<KIND>, dim3(grid), dim3(kThreads), 0, s, iters, out);
@@ -190,6 +228,14 @@ int fp4q_probe_stream(int kind, const void* src, void* dst, int64_t n16, int gri
     case 8: hipLaunchKernelGGL((k_copy<8, true>), dim3(grid), dim3(kThreads), 0, s, in, out, n16); break;
     default: return -1;
     }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int fp4q_probe_fp4_convert(unsigned long long* mismatches, void* stream) {
+    if (!mismatches) return -1;
+    const uint64_t threads = (1ull << 32) / 64u;
+    hipLaunchKernelGGL(k_fp4_convert, dim3((unsigned)(threads / kThreads)), dim3(kThreads), 0, (hipStream_t)stream,
+                       mismatches);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

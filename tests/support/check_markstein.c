@@ -64,3 +64,38 @@ int check_markstein(uint32_t mant_lo, uint32_t mant_hi, int radius, uint64_t* n_
     *quot_mismatch = qm;
     return bad;
 }
+
+/* The same quotient for the scale code of a block, s = RNE_E4M3(fl(a / d))
+ * (E4M3, UE5M3) with d = fl(6 g) or fl(4 g) and R = fl(1/d) computed once
+ * per call.  The 3-bit-mantissa rounding of two adjacent fp32 quotients can
+ * only differ when one of them is a grid point or a midpoint of that
+ * format; relative to their binade these are the values 1 + k/16, k = 0..15
+ * (the subnormal codes of both formats land on the same relative values).
+ * Every divisor mantissa and every dividend within `radius` ulps of
+ * fl((1 + k/16) d) is checked: the quotients must be identical. */
+int check_markstein_scale(uint32_t mant_lo, uint32_t mant_hi, int radius, uint64_t* n_checked)
+{
+    int bad = 0;
+    uint64_t n = 0;
+    for (uint32_t m = mant_lo; m < mant_hi; ++m) {
+        float S = fb(0x3F800000u | m);
+        float R = 1.0f / S;
+        for (int k = 0; k < 16; ++k) {
+            uint32_t c = bf((1.0f + (float)k / 16.0f) * S);
+            for (int d = -radius; d <= radius; ++d) {
+                float a = fb(c + d);
+                float ref = a / S;
+                float q0 = a * R;
+                float r = fmaf(-q0, S, a);
+                float q = fmaf(r, R, q0);
+                ++n;
+                if (q != ref) {
+                    if (bad < 10) printf("scale quotient mismatch S=%a a=%a ref=%a q=%a\n", S, a, ref, q);
+                    ++bad;
+                }
+            }
+        }
+    }
+    *n_checked = n;
+    return bad;
+}

@@ -41,3 +41,26 @@ def test_bins_agree_for_every_scale_mantissa(checker):
     assert checked == (1 << 23) * 8 * 13
     assert bad == 0
     assert sum(r[2] for r in res) == 0       # the quotients themselves agree
+
+
+def test_scale_code_quotient_for_every_divisor_mantissa(checker):
+    """The block scale code rounds fl(a_b / fl(M g)) to a 3-bit mantissa
+    (E4M3, UE5M3); the kernels form that quotient from fl(1 / fl(M g)) with
+    the same two FMAs.  Around every grid point and midpoint of such a format
+    (relative values 1 + k/16) and for every divisor mantissa, the quotients
+    must equal the IEEE division's."""
+    checker.check_markstein_scale.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
+                                              ctypes.POINTER(ctypes.c_uint64)]
+    checker.check_markstein_scale.restype = ctypes.c_int
+    parts = 16
+    step = (1 << 23) // parts
+
+    def run(i):
+        n = ctypes.c_uint64(0)
+        bad = checker.check_markstein_scale(i * step, (i + 1) * step, 6, ctypes.byref(n))
+        return bad, n.value
+
+    with ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(run, range(parts)))
+    assert sum(r[1] for r in res) == (1 << 23) * 16 * 13
+    assert sum(r[0] for r in res) == 0
