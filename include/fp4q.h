@@ -33,7 +33,8 @@
  *            effective block scale is S = fl(decode(code) * g).  For E8M0
  *            there is no g (it is 1); UE5M3 takes g from NONE or USER only.
  *  - Every buffer is device memory the caller allocated (the library
- *    allocates nothing and keeps no state).  Base pointers must be 16-byte
+ *    allocates nothing and keeps no state; the one exception is the static
+ *    scratch array of fp4q_quantize_noalloc).  Base pointers must be 16-byte
  *    aligned, and ld * element_size must be a multiple of 16 bytes, as must
  *    cols * element_size.  Element types: fp32, bf16, fp16.
  *  - `stream` is a hipStream_t (NULL = the default stream).  A call only
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 5
+#define FP4Q_ABI_VERSION 6
 
 typedef enum {
     FP4Q_OK = 0,
@@ -68,7 +69,9 @@ typedef enum {
                                  with GIVEN */
     FP4Q_ERR_SHAPE = 3,       /* block / rotation / sub-block does not tile the row */
     FP4Q_ERR_ALIGNMENT = 4,   /* base pointer or row pitch not 16-byte aligned */
-    FP4Q_ERR_DEVICE = 5       /* the HIP runtime refused a launch */
+    FP4Q_ERR_DEVICE = 5,      /* the HIP runtime refused a launch */
+    FP4Q_ERR_TOO_LARGE = 6    /* fp4q_quantize_noalloc: the workspace this call needs
+                                 exceeds the library's static scratch */
 } fp4q_status;
 
 typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1, FP4Q_F16 = 2 } fp4q_dtype;
@@ -164,6 +167,23 @@ fp4q_status fp4q_quantize(const fp4q_config* cfg, const void* x, int x_dt, int64
                           int64_t cols, int64_t ld_x, uint8_t* codes, uint8_t* scales,
                           float* g_dev, void* dequant, int dq_dt, int64_t ld_dq,
                           float* block_mse, void* workspace, void* stream);
+
+/* fp4q_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and errors, without `workspace`.  The workspace
+ * lives in a static device array of 16 MiB inside the library (one per GPU,
+ * held until the process ends); a call never calls hipMalloc, hipFree or any
+ * allocating routine.  A configuration and shape whose fp4q_workspace_bytes
+ * exceeds 16 MiB (only GLOBAL_SEARCH on tensors of more than about 4 M
+ * 16-value units) returns FP4Q_ERR_TOO_LARGE and enqueues nothing.  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (other streams, other host threads) race and must be ordered by the
+ * caller.  Nothing in the array needs to start at zero (each call writes
+ * every entry it reads). */
+fp4q_status fp4q_quantize_noalloc(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows,
+                                  int64_t cols, int64_t ld_x, uint8_t* codes, uint8_t* scales,
+                                  float* g_dev, void* dequant, int dq_dt, int64_t ld_dq,
+                                  float* block_mse, void* stream);
 
 /* Dequantize codes + scales to out [rows, ld_out] (type out_dt):
  * (-1)^s fl(grid[mag] * S) with S = fl(decode(scale) * g); g is read from

@@ -7,10 +7,18 @@
 
 #include "fp4q.h"
 #include <algorithm>
+#include <mutex>
 
 #include "fp4q_launch.hpp"
 
 using namespace fp4q_dev;
+
+// Workspace of fp4q_quantize_noalloc: one copy per device, held until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol); it takes the device address that
+// hipGetSymbolAddress returns for the device in use.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -77,6 +85,35 @@ fp4q_status check_buffer(const void* p) {
 
 fp4q_status device_status(hipError_t e) { return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_DEVICE; }
 
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream), looked up once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+fp4q_status scratch_address(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return FP4Q_ERR_DEVICE;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return FP4Q_ERR_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return FP4Q_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return FP4Q_ERR_DEVICE;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return FP4Q_ERR_DEVICE;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !ptr) return FP4Q_ERR_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FP4Q_OK;
+}
+
 int unit_of(int x_dt, int block, int H) {
     int u = 16 / elem_size(x_dt);
     if (block > u) u = block;
@@ -102,10 +139,12 @@ size_t search_workspace_bytes(int64_t tiles) {
     } while (0)
 
 // Shared body of fp4q_quantize and fp4q_scale_search.
+// from_scratch: the workspace is the static scratch (fp4q_quantize_noalloc),
+// looked up after every argument check.
 fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,
                       int64_t ld_x, uint8_t* codes, uint8_t* scales, float* g_dev, void* dequant,
                       int dq_dt, int64_t ld_dq, float* mse, float* sse, void* workspace,
-                      void* stream) {
+                      void* stream, bool from_scratch = false) {
     const int B = cfg->block, H = cfg->hadamard;
     FP4Q_TRY(check_dims(rows, cols, B, H));
     const bool need_g = cfg->global_mode != FP4Q_GLOBAL_NONE;
@@ -127,6 +166,7 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
     if (sse) FP4Q_TRY(check_buffer(sse));
     const bool search = cfg->global_mode == FP4Q_GLOBAL_SEARCH;
     const bool tamax = cfg->global_mode == FP4Q_GLOBAL_TENSOR_AMAX || search;
+    if (tamax && from_scratch) FP4Q_TRY(scratch_address(s, &workspace));
     if (tamax) FP4Q_TRY(check_buffer(workspace));
 
     if (tamax) {
@@ -237,6 +277,7 @@ const char* fp4q_status_string(int status) {
     case FP4Q_ERR_SHAPE: return "shape does not tile into blocks";
     case FP4Q_ERR_ALIGNMENT: return "pointer or row pitch not 16-byte aligned";
     case FP4Q_ERR_DEVICE: return "device launch failed";
+    case FP4Q_ERR_TOO_LARGE: return "workspace needed exceeds the library's static scratch";
     }
     return "unknown status";
 }
@@ -258,6 +299,16 @@ fp4q_status fp4q_quantize(const fp4q_config* cfg, const void* x, int x_dt, int64
     if (!codes && rows > 0 && cols > 0) return FP4Q_ERR_INVALID_ARG;
     return run_quant(cfg, x, x_dt, rows, cols, ld_x, codes, scales, g_dev, dequant, dq_dt, ld_dq,
                      block_mse, nullptr, workspace, stream);
+}
+
+fp4q_status fp4q_quantize_noalloc(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,
+                                  int64_t ld_x, uint8_t* codes, uint8_t* scales, float* g_dev, void* dequant,
+                                  int dq_dt, int64_t ld_dq, float* block_mse, void* stream) {
+    FP4Q_TRY(check_config(cfg));
+    if (!codes && rows > 0 && cols > 0) return FP4Q_ERR_INVALID_ARG;
+    if (fp4q_workspace_bytes(cfg, rows, cols) > kNoAllocScratchBytes) return FP4Q_ERR_TOO_LARGE;
+    return run_quant(cfg, x, x_dt, rows, cols, ld_x, codes, scales, g_dev, dequant, dq_dt, ld_dq, block_mse,
+                     nullptr, nullptr, stream, true);
 }
 
 fp4q_status fp4q_scale_search(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows,

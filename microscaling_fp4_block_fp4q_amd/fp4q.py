@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(PKG, "libfp4q.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "fp4q.h")
 
 # FP4Q_ABI_VERSION and the enums (include/fp4q.h)
-ABI_VERSION = 5
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE = range(6)
+ABI_VERSION = 6
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE, ERR_TOO_LARGE = range(7)
 F32, BF16, F16 = 0, 1, 2
 E8M0, E4M3, UE5M3 = 0, 1, 2
 ABSMAX, PREVENT_ZERO, FOUR_OVER_SIX, BRUTE_FORCE, GIVEN = range(5)
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.fp4q_workspace_bytes.argtypes = [cp, i64, i64]
         L.fp4q_quantize.restype = ctypes.c_int
         L.fp4q_quantize.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, p, ctypes.c_int, i64, p, p, p]
+        L.fp4q_quantize_noalloc.restype = ctypes.c_int
+        L.fp4q_quantize_noalloc.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, p, ctypes.c_int, i64, p, p]
         L.fp4q_dequantize.restype = ctypes.c_int
         L.fp4q_dequantize.argtypes = [cp, p, p, p, i64, i64, p, ctypes.c_int, i64, p]
         L.fp4q_block_mse.restype = ctypes.c_int
@@ -227,6 +229,24 @@ def fp4q_quantize(cfg, x, codes, scales, g=None, dequant=None, block_mse=None, w
                              _ptr(scales), _ptr(g), _ptr(dequant), dq_dt, ld_dq, _ptr(block_mse),
                              _ptr(workspace), _stream(stream))
     _check(st, "fp4q_quantize")
+
+
+def fp4q_quantize_noalloc(cfg, x, codes, scales, g=None, dequant=None, block_mse=None, stream=None):
+    """fp4q_quantize with the workspace in the library's static device scratch."""
+    rows, cols, ld = _rows_cols_ld(x)
+    nb = cols // cfg.block
+    _dense(codes, torch.uint8, (rows, cols // 2), "codes")
+    _dense(scales, torch.uint8, (rows, nb), "scales")
+    _dense(block_mse, torch.float32, (rows, nb), "block_mse")
+    _scalar_g(g)
+    dq_dt, ld_dq = F32, cols
+    if dequant is not None:
+        ld_dq = _out_2d(dequant, rows, cols, "dequant")
+        dq_dt = dtype_code(dequant)
+    st = lib().fp4q_quantize_noalloc(ctypes.byref(cfg), _ptr(x), dtype_code(x), rows, cols, ld, _ptr(codes),
+                                     _ptr(scales), _ptr(g), _ptr(dequant), dq_dt, ld_dq, _ptr(block_mse),
+                                     _stream(stream))
+    _check(st, "fp4q_quantize_noalloc")
 
 
 def fp4q_scale_search(cfg, x, scales, g=None, best_sse=None, workspace=None, stream=None):

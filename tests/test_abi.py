@@ -40,7 +40,7 @@ def test_version_strings_workspace():
     hdr = open(F.HEADER).read()
     declared = int(re.search(r"#define FP4Q_ABI_VERSION (\d+)", hdr).group(1))
     assert F.abi_version() == declared == F.ABI_VERSION
-    for s in range(6):
+    for s in range(7):
         assert F.status_string(s) and F.status_string(s) != "unknown status"
     assert F.status_string(99) == "unknown status"
     assert F.workspace_bytes(F.nvfp4(), 4096, 4096) >= 4
@@ -179,3 +179,25 @@ def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(F, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         F.lib()
+
+
+def quant_noalloc(cfg, x=A, x_dt=F.F32, rows=16, cols=64, ld=64, codes=A, scales=A, g=A, dq=None, dq_dt=F.F32,
+                  ld_dq=64, mse=None):
+    return F.lib().fp4q_quantize_noalloc(ctypes.byref(cfg) if cfg is not None else None, P(x), x_dt, rows, cols,
+                                         ld, P(codes), P(scales), P(g), P(dq), dq_dt, ld_dq, P(mse), None)
+
+
+@needs_lib
+@cpu_only
+def test_quantize_noalloc_validation():
+    """The allocation-free quantize: the same argument checks, and a
+    workspace beyond the static scratch (16 MiB) is refused before any
+    device call."""
+    assert quant_noalloc(None) == F.ERR_INVALID_ARG
+    assert quant_noalloc(F.config(1, 12)) == F.ERR_SHAPE
+    assert quant_noalloc(F.nvfp4(), codes=0) == F.ERR_INVALID_ARG
+    assert quant_noalloc(F.nvfp4(), x=A + 4) == F.ERR_ALIGNMENT
+    search = F.config(F.E4M3, 4, F.ABSMAX, F.GLOBAL_SEARCH)
+    assert F.workspace_bytes(search, 8192, 8192) > 16 << 20
+    assert quant_noalloc(search, rows=8192, cols=8192, ld=8192) == F.ERR_TOO_LARGE
+    assert F.status_string(F.ERR_TOO_LARGE) != "unknown status"
