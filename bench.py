@@ -61,7 +61,8 @@ FLUSH_MIB = 1024                            # the cold leg reads 1 GiB before ea
 
 STRATS = {0: "absmax", 1: "prevent-zero", 2: "4-over-6", 3: "brute-force"}
 VALU_PROBES = {0: "v_add_f32", 1: "v_mul_f32", 2: "v_fma_f32", 3: "integer add/xor/shift",
-               4: "fp32 min/max/add", 5: "brute-force candidate evaluation (block of 16)"}
+               4: "fp32 min/max/add", 5: "brute-force candidate evaluation (block of 16)",
+               6: "brute-force candidate evaluation, rounding by the FP4 pair converts"}
 
 
 def parse(argv=None):

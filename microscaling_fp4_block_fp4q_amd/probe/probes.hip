@@ -20,7 +20,8 @@
 //       2: v_fma_f32; 3: integer add / xor / shift; 4: fp32 min / max / add;
 //       5: the candidate evaluation of the brute-force scale search (division-
 //       free quotient at a scale read from LDS, E2M1 rounding, dequantized
-//       product, difference, square, balanced-tree sum over a block of 16).
+//       product, difference, square, balanced-tree sum over a block of 16);
+//       6: the same with the rounding by the hardware FP4 pair converts.
 //       The executed instruction count comes from the SQ_INSTS_VALU counter.
 //
 //   int fp4q_probe_fp4_convert(unsigned long long* mismatches, void* stream);
@@ -137,6 +138,40 @@ __global__ __launch_bounds__(kThreads) void k_valu(int iters, float* out) {
 #pragma unroll
             for (int c = 0; c < kChains; ++c) x[c] = fminf(fmaxf(x[c], lo), hi) + d;
         }
+    } else if constexpr (KIND == 6) {
+        // the same evaluation with the E2M1 rounding done by the hardware FP4
+        // pair converts (fp32 -> FP4 -> fp32)
+        __shared__ float2 s_tab[128];
+        if (threadIdx.x < 128) {
+            const float S = 0.0625f + 0.015625f * (float)threadIdx.x;
+            s_tab[threadIdx.x] = make_float2(S, 1.0f / S);
+        }
+        __syncthreads();
+        float acc = 0.0f;
+#pragma unroll 1
+        for (int it = 0; it < iters; ++it) {
+            const float2 sr = s_tab[it & 127];
+            float q[kChains], e[kChains];
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+                const float a = x[c];
+                const float q0 = a * sr.y;
+                const float rr = __builtin_fmaf(-q0, sr.x, a);
+                q[c] = __builtin_fmaf(rr, sr.y, q0);
+            }
+#pragma unroll
+            for (int c = 0; c < kChains; c += 2) {
+                const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[c], q[c + 1], 1.0f, 0);
+                const auto g2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float d = x[c + h] - g2[h] * sr.x;
+                    e[c + h] = d * d;
+                }
+            }
+            acc = fminf(acc, tree_sum<kChains>(e));
+        }
+        x[0] += acc;
     } else {
         // the brute-force candidate evaluation: a block of 16 values at scale
         // S_it (one LDS broadcast per candidate), as the search kernels run it
@@ -250,6 +285,7 @@ int fp4q_probe_valu(int kind, int iters, int grid, float* out, void* stream) {
     case 3: e = launch_valu<3>(iters, grid, out, s); break;
     case 4: e = launch_valu<4>(iters, grid, out, s); break;
     case 5: e = launch_valu<5>(iters, grid, out, s); break;
+    case 6: e = launch_valu<6>(iters, grid, out, s); break;
     default: return -1;
     }
     return e == hipSuccess ? 0 : -1;
