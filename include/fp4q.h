@@ -47,7 +47,9 @@
  *    that block a NaN block: NaN scale code, zero-magnitude codes carrying
  *    the element signs, NaN dequantized values (0x7FC00000 with the element
  *    sign), NaN MSE.  A scale that decodes to NaN, infinity or a negative
- *    value (possible with a caller's g) gives a NaN block as well.
+ *    value (possible with a caller's g) gives a NaN block as well.  With a
+ *    rotation, every NaN the rotation produces counts as positive (IEEE 754
+ *    leaves the sign of a NaN returned by arithmetic unspecified).
  *  - Results are deterministic and independent of the launch shape.
  */
 #ifndef FP4Q_H

@@ -365,8 +365,13 @@ __device__ __forceinline__ T tree_sum(const T (&v)[M]) {
 // ---------------------------------------------------------------------------
 // Block-wise normalised Walsh-Hadamard transform in registers (MR-GPTQ page,
 // sections 2.1-2.3): Sylvester order, radix-2 butterflies with stride
-// h = 1, 2, ..., H/2, then one multiplication by fl(1/sqrt(H)).
+// h = 1, 2, ..., H/2, then one multiplication by fl(1/sqrt(H)).  A NaN the
+// transform produces leaves as the positive quiet NaN: IEEE 754 leaves the
+// sign of an arithmetic NaN open (gfx950's subtraction flips it where x86's
+// keeps it), and the sign of a NaN element reaches its code nibble.
 // ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float rotated_nan_canonical(float v) { return v == v ? v : as_f(kQNaN); }
 
 template <int H>
 __device__ __forceinline__ constexpr float hadamard_coef() {
@@ -393,7 +398,7 @@ __device__ __forceinline__ void fwht_segments(float (&y)[U]) {
     }
     constexpr float c = hadamard_coef<H>();
 #pragma unroll
-    for (int i = 0; i < U; ++i) y[i] = y[i] * c;
+    for (int i = 0; i < U; ++i) y[i] = rotated_nan_canonical(y[i] * c);
 }
 
 }  // namespace fp4q_dev

@@ -66,7 +66,8 @@ __device__ __forceinline__ float group_tree_sum(float v) {
 // stride h < E run inside the lane, the stages with h >= E pair lane l with
 // lane l ^ (h / E).  The lower element of a pair becomes fl(a + b), the
 // upper fl(a - b), a the lower and b the upper value, as in the in-lane
-// stages; then every value is multiplied once by fl(1 / sqrt(H)).
+// stages; then every value is multiplied once by fl(1 / sqrt(H)) (a NaN
+// leaves as the positive quiet NaN, as in fwht_segments).
 template <int H, int E>
 __device__ __forceinline__ void fwht_chunk(float (&y)[E], int lane) {
     static_assert(H % E == 0 && H / E <= 8, "segments of 1 to 8 chunks");
@@ -96,7 +97,7 @@ __device__ __forceinline__ void fwht_chunk(float (&y)[E], int lane) {
     });
     constexpr float c = hadamard_coef<H>();
 #pragma unroll
-    for (int i = 0; i < E; ++i) y[i] = y[i] * c;
+    for (int i = 0; i < E; ++i) y[i] = rotated_nan_canonical(y[i] * c);
 }
 
 // ---------------------------------------------------------------------------

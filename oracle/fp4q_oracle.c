@@ -404,16 +404,22 @@ static int choose_scale(int fmt, int strategy, const float* y, int B, float g, i
 /* ------------------------------------------------------------------------ */
 
 /* Widen a [rows, cols] tensor with row stride ld to a dense fp32 copy and
- * rotate each contiguous segment of H values when H != 0. */
+ * rotate each contiguous segment of H values when H != 0.  A NaN the
+ * rotation produces is taken as the positive quiet NaN: IEEE 754 does not
+ * fix the sign of a NaN that arithmetic returns, and that sign would reach
+ * the sign bit of the element's code. */
 static float* widen_and_rotate(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld, int H)
 {
     float* y = (float*)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
     if (!y) return NULL;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) y[r * cols + c] = load_elem(x, dt, r * ld + c);
-    if (H > 0)
+    if (H > 0) {
         for (int64_t r = 0; r < rows; ++r)
             for (int64_t c = 0; c < cols; c += H) oracle_fwht(y + r * cols + c, H);
+        for (int64_t i = 0; i < rows * cols; ++i)
+            if (isnan(y[i])) y[i] = canonical_nan(0);
+    }
     return y;
 }
 
