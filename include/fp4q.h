@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 6
+#define FP4Q_ABI_VERSION 7
 
 typedef enum {
     FP4Q_OK = 0,
@@ -169,6 +169,29 @@ fp4q_status fp4q_quantize(const fp4q_config* cfg, const void* x, int x_dt, int64
                           int64_t cols, int64_t ld_x, uint8_t* codes, uint8_t* scales,
                           float* g_dev, void* dequant, int dq_dt, int64_t ld_dq,
                           float* block_mse, void* workspace, void* stream);
+
+/* fp4q_quantize that also counts the codes it writes: the codebook
+ * occupancy of the TORQ page, section 2.B (how evenly the 16 FP4 codewords
+ * are used; their collapse onto the smallest magnitudes is what it
+ * measures), fused into the quantize kernels instead of a second pass over
+ * the codes.  counts [FP4Q_COUNT_REPLICAS][16] device uint64, dense,
+ * ACCUMULATED: the number of written nibbles equal to c (sign bit 3, E2M1
+ * magnitude bits 0-2), NaN blocks included (their nibbles carry only the
+ * sign), is added to column c, split over the rows in a way that depends
+ * on the launch; the occupancy of code c is the sum of column c.  The rows
+ * spread the kernels' final atomic additions over separate 128-byte lines
+ * (128-byte alignment keeps each row on one line): additions from many
+ * workgroups to one line serialise.  Zero counts before the first call.
+ * The codes, scales, g, dequant and MSE are those fp4q_quantize writes.
+ * counts is required (FP4Q_ERR_INVALID_ARG) and 8-byte aligned
+ * (FP4Q_ERR_ALIGNMENT); every other argument as for fp4q_quantize.  The
+ * column sums are integers, exact whatever the order of the additions. */
+#define FP4Q_COUNT_REPLICAS 64
+fp4q_status fp4q_quantize_histogram(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows,
+                                    int64_t cols, int64_t ld_x, uint8_t* codes, uint8_t* scales,
+                                    float* g_dev, void* dequant, int dq_dt, int64_t ld_dq,
+                                    float* block_mse, uint64_t* counts, void* workspace,
+                                    void* stream);
 
 /* fp4q_quantize for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

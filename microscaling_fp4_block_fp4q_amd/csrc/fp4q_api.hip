@@ -13,6 +13,8 @@
 
 using namespace fp4q_dev;
 
+static_assert(FP4Q_COUNT_REPLICAS == kCountReplicas, "rows of the fused code counts");
+
 // Workspace of fp4q_quantize_noalloc: one copy per device, held until the
 // process ends.  Host code never passes this name to a kernel (on the host it
 // is only a stand-in for the symbol); it takes the device address that
@@ -140,11 +142,12 @@ size_t search_workspace_bytes(int64_t tiles) {
 
 // Shared body of fp4q_quantize and fp4q_scale_search.
 // from_scratch: the workspace is the static scratch (fp4q_quantize_noalloc),
-// looked up after every argument check.
+// looked up after every argument check.  counts: code occupancy to add to
+// (fp4q_quantize_histogram), checked by the caller.
 fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows, int64_t cols,
                       int64_t ld_x, uint8_t* codes, uint8_t* scales, float* g_dev, void* dequant,
                       int dq_dt, int64_t ld_dq, float* mse, float* sse, void* workspace,
-                      void* stream, bool from_scratch = false) {
+                      void* stream, bool from_scratch = false, unsigned long long* counts = nullptr) {
     const int B = cfg->block, H = cfg->hadamard;
     FP4Q_TRY(check_dims(rows, cols, B, H));
     const bool need_g = cfg->global_mode != FP4Q_GLOBAL_NONE;
@@ -246,6 +249,7 @@ fp4q_status run_quant(const fp4q_config* cfg, const void* x, int x_dt, int64_t r
     qa.g_in = g_dev;
     if (search) qa.g_out = nullptr;      // g_dev already holds the searched scale
     qa.prevent_zero = cfg->strategy == FP4Q_PREVENT_ZERO;
+    qa.counts = counts;
     const int grid = grid_for(qa.units);
     hipError_t e;
     switch (x_dt) {
@@ -309,6 +313,18 @@ fp4q_status fp4q_quantize_noalloc(const fp4q_config* cfg, const void* x, int x_d
     if (fp4q_workspace_bytes(cfg, rows, cols) > kNoAllocScratchBytes) return FP4Q_ERR_TOO_LARGE;
     return run_quant(cfg, x, x_dt, rows, cols, ld_x, codes, scales, g_dev, dequant, dq_dt, ld_dq, block_mse,
                      nullptr, nullptr, stream, true);
+}
+
+fp4q_status fp4q_quantize_histogram(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows,
+                                    int64_t cols, int64_t ld_x, uint8_t* codes, uint8_t* scales, float* g_dev,
+                                    void* dequant, int dq_dt, int64_t ld_dq, float* block_mse, uint64_t* counts,
+                                    void* workspace, void* stream) {
+    FP4Q_TRY(check_config(cfg));
+    if (!counts) return FP4Q_ERR_INVALID_ARG;
+    if ((uintptr_t)counts & 7u) return FP4Q_ERR_ALIGNMENT;
+    if (!codes && rows > 0 && cols > 0) return FP4Q_ERR_INVALID_ARG;
+    return run_quant(cfg, x, x_dt, rows, cols, ld_x, codes, scales, g_dev, dequant, dq_dt, ld_dq, block_mse,
+                     nullptr, workspace, stream, false, reinterpret_cast<unsigned long long*>(counts));
 }
 
 fp4q_status fp4q_scale_search(const fp4q_config* cfg, const void* x, int x_dt, int64_t rows,

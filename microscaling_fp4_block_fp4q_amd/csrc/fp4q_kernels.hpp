@@ -59,6 +59,7 @@ struct QuantArgs {
     float user_g;
     const float* g_in;      // GM_DEVICE: the scale to use
     int prevent_zero;
+    unsigned long long* counts;   // [16] code occupancy to add to, or null
 };
 
 // Per-tensor scale search: block SSE totals of every candidate, per tile.
@@ -194,6 +195,73 @@ __device__ __forceinline__ int64_t unit_offset(int64_t u, int64_t upr, int64_t l
     if (contiguous) return u * U;
     int64_t row = u / upr;
     return row * ld + (u - row * upr) * U;
+}
+
+// ---------------------------------------------------------------------------
+// Code occupancy counted while quantizing (TORQ page, section 2.B: how often
+// each of the 16 FP4 codewords is used).  Counters are private per thread
+// while a kernel runs; each workgroup adds its 16 totals, once, at the end,
+// to one of kCountReplicas rows of the caller's 64-bit counts (row =
+// workgroup index mod kCountReplicas).  Atomic additions from many
+// workgroups to one 128-byte line serialise at several ns each; with every
+// workgroup on the same line the resident grid's final additions took
+// longer than a whole quantize call, spread over 64 lines they overlap.
+// ---------------------------------------------------------------------------
+
+constexpr int kCountReplicas = 64;   // rows of 16 counts (FP4Q_COUNT_REPLICAS)
+
+// Adds to cnt[v], for every v, the number of the eight nibbles of w equal to
+// v.  Bit j of every nibble is sliced out to bit 4k of b[j]; the mask of the
+// nibbles equal to v is the AND of four slices or their complements (shared
+// as two pair products), and one popcount adds it.
+__device__ __forceinline__ void count_nibbles(uint32_t w, uint32_t (&cnt)[16]) {
+    constexpr uint32_t M = 0x11111111u;
+    uint32_t b[4], nb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        b[j] = (w >> j) & M;
+        nb[j] = b[j] ^ M;
+    }
+    const uint32_t lo[4] = {nb[1] & nb[0], nb[1] & b[0], b[1] & nb[0], b[1] & b[0]};   // bits 1..0 = v & 3
+    const uint32_t hi[4] = {nb[3] & nb[2], nb[3] & b[2], b[3] & nb[2], b[3] & b[2]};   // bits 3..2 = v >> 2
+#pragma unroll
+    for (int v = 0; v < 16; ++v) cnt[v] += (uint32_t)__popc(hi[v >> 2] & lo[v & 3]);
+}
+
+// Adds the workgroup's totals of one code per thread to its row of counts:
+// thread t holds part (its partial count of code t & 15).  Every thread of
+// the workgroup calls it; one 64-bit atomic per nonzero code per workgroup.
+__device__ __forceinline__ void add_code_counts(uint32_t part, unsigned long long* counts) {
+    __shared__ unsigned long long s_part[kThreads / 64][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned long long v = part;
+    v += __shfl_xor(v, 16, 64);                   // the four lanes of a wave with the same code
+    v += __shfl_xor(v, 32, 64);
+    if (lane < 16) s_part[wave][lane] = v;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        unsigned long long total = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) total += s_part[w][threadIdx.x];
+        if (total) atomicAdd(&counts[(blockIdx.x % kCountReplicas) * 16 + threadIdx.x], total);
+    }
+}
+
+// Workgroup flush of 16 per-thread register counters (cnt[v] of every
+// thread): thread t first gathers code t & 15 from the 16 threads of its
+// group of 16 lanes.
+__device__ __forceinline__ void flush_code_counts(const uint32_t (&cnt)[16], unsigned long long* counts) {
+    const int lane = threadIdx.x & 63;
+    uint32_t part = 0;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        // sum of cnt[v] over the 16 lanes of this lane's group; lane v of the group keeps it
+        uint32_t c = cnt[v];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) c += (uint32_t)__shfl_xor((int)c, o, 64);
+        part = (lane & 15) == v ? c : part;
+    }
+    add_code_counts(part, counts);
 }
 
 // ---------------------------------------------------------------------------
@@ -1015,8 +1083,9 @@ __device__ __forceinline__ void bf_load_tile(const P& p, int64_t u0, int nvalid,
 }
 
 // Brute-force quantize: bf_search_tile per tile, then every lane encodes its
-// blocks at the winning codes and stores the outputs.
-template <class InT, int B, int H, int SF>
+// blocks at the winning codes and stores the outputs.  CNT: also count the
+// written codes into p.counts (register counters per thread).
+template <class InT, int B, int H, int SF, bool CNT>
 __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
     constexpr int U = unit_elems<InT, B, H>();
     constexpr int NB = U / B;
@@ -1053,6 +1122,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             for (int i = 0; i < U; ++i) ynext[i] = 0.0f;
         }
     };
+    uint32_t cnt[16];                     // code occupancy of this thread (CNT)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) cnt[v] = 0u;
+    // units of 4 values fill half a code word: two tiles' words are counted together
+    uint32_t pend = 0u;
+    bool have_pend = false;
     if constexpr (PREFETCH) fetch((int64_t)blockIdx.x * (kThreads / 64) + wave);
     for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave; t < ntiles; t += tstride) {
         const int64_t u0 = t * kTileUnits;
@@ -1101,6 +1176,26 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             finish_block<B, b * B>(y, r, S, nan_blk[b], cw, sink);
         });
         store_unit_outputs<B, U>(p, u0, nvalid, lane, W.tile, cw, sc, sse, true);
+        if constexpr (CNT) {
+            if (active) {
+                if constexpr (U == 4) {
+                    if (have_pend) count_nibbles(pend | (cw[0] << 16), cnt);
+                    pend = cw[0];
+                    have_pend = !have_pend;
+                } else {
+                    static_assert(U % 8 == 0, "units of 4 or of whole code words");
+#pragma unroll
+                    for (int i = 0; i < code_words(U); ++i) count_nibbles(cw[i], cnt);
+                }
+            }
+        }
+    }
+    if constexpr (CNT) {
+        if (have_pend) {
+            count_nibbles(pend, cnt);
+            cnt[0] -= 4u;                     // the empty high half of the word
+        }
+        flush_code_counts(cnt, p.counts);
     }
 }
 

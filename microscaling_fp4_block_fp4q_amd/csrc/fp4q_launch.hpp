@@ -76,7 +76,8 @@ constexpr int kBfMaxWorkgroupsPerCU = 6;
 template <class InT, int B, int H, int SF, int ST>
 hipError_t launch_quant_t(const QuantArgs& a, int grid, hipStream_t s) {
     if constexpr (ST == ST_BRUTE_FORCE) {
-        return launch_resident<k_quant_bf<InT, B, H, SF>, kBfMaxWorkgroupsPerCU>(a, grid, s);
+        if (a.counts) return launch_resident<k_quant_bf<InT, B, H, SF, true>, kBfMaxWorkgroupsPerCU>(a, grid, s);
+        return launch_resident<k_quant_bf<InT, B, H, SF, false>, kBfMaxWorkgroupsPerCU>(a, grid, s);
     } else {
         constexpr int R = stream_rounds<InT>();
         const int64_t per_wg = (int64_t)kThreads * R;

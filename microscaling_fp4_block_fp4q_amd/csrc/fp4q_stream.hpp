@@ -399,6 +399,12 @@ constexpr int stream_rounds() { return 2; }
 // operations in flight and wait only for the ones a value needs.  Every lane
 // of a block stores the block's scale and error (the same value to the same
 // address), which keeps those stores unconditional too.
+//
+// With p.counts the written codes are also counted: 16 counters per thread
+// in LDS (code n of thread t at n * kThreads + t, so a wave's increments
+// fall on distinct banks), one LDS add per code, summed per workgroup at
+// the end.  The 16 KiB this takes leave the occupancy unchanged (eight
+// workgroups per compute unit still fit).
 template <class InT, int B, int H, int SF, int ST, int R>
 __global__ __launch_bounds__(kThreads) void k_qstream(QuantArgs p) {
     constexpr int ES = ElemSize<InT>::value;
@@ -422,6 +428,14 @@ __global__ __launch_bounds__(kThreads) void k_qstream(QuantArgs p) {
         __shared__ ScaleTab s_tab;
         fill_scale_tab<SF>(s_tab, g);
         cx.tab = &s_tab;
+    }
+
+    __shared__ uint32_t s_bins[16 * kThreads];
+    const bool counting = p.counts != nullptr;
+    uint32_t* bins = s_bins + threadIdx.x;        // only this thread touches them until the end
+    if (counting) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bins[v * kThreads] = 0u;
     }
 
     const int64_t nchunks = p.units;              // rows * cols / E (>= 1)
@@ -470,6 +484,10 @@ __global__ __launch_bounds__(kThreads) void k_qstream(QuantArgs p) {
             if (!FULL && j >= nchunks) continue;
             const int64_t e0 = j * E;                 // dense element index of the chunk
             if (p.codes) store_code_word<E>(p.codes, e0, cw);
+            if (counting) {
+#pragma unroll
+                for (int i = 0; i < E; ++i) atomicAdd(&bins[((cw >> (4 * i)) & 15u) * kThreads], 1u);
+            }
             if (p.dq) store_dq_chunk<E>(p.dq, p.dq_dt, chunk_offset<E>(j, cpr, p.ld_dq, dq_contig), dq);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
@@ -485,16 +503,26 @@ __global__ __launch_bounds__(kThreads) void k_qstream(QuantArgs p) {
     };
 
     int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave;
-    if (t >= ntrips) return;
-    Trip cur;
-    fetch(t, cur);
-    for (; t < nfull; t += tstride) {
-        Trip nxt;
-        fetch(t + tstride, nxt);
-        process(cur, t, IC<1>{});
-        cur = nxt;
+    if (t < ntrips) {
+        Trip cur;
+        fetch(t, cur);
+        for (; t < nfull; t += tstride) {
+            Trip nxt;
+            fetch(t + tstride, nxt);
+            process(cur, t, IC<1>{});
+            cur = nxt;
+        }
+        if (t < ntrips) process(cur, t, IC<0>{});     // the last, partial trip
     }
-    if (t < ntrips) process(cur, t, IC<0>{});     // the last, partial trip
+    if (counting) {
+        // thread t gathers code t & 15 from the 16 threads of its group of 16
+        __syncthreads();
+        const int code = threadIdx.x & 15, seg = threadIdx.x >> 4;
+        uint32_t part = 0;
+#pragma unroll
+        for (int l = 0; l < 16; ++l) part += s_bins[code * kThreads + seg * 16 + l];
+        add_code_counts(part, p.counts);
+    }
 }
 
 // Partial per-tensor abs-max (of the rotated values when H != 0) for

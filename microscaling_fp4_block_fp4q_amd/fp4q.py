@@ -22,12 +22,13 @@ LIB_PATH = os.path.join(PKG, "libfp4q.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "fp4q.h")
 
 # FP4Q_ABI_VERSION and the enums (include/fp4q.h)
-ABI_VERSION = 6
+ABI_VERSION = 7
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE, ERR_TOO_LARGE = range(7)
 F32, BF16, F16 = 0, 1, 2
 E8M0, E4M3, UE5M3 = 0, 1, 2
 ABSMAX, PREVENT_ZERO, FOUR_OVER_SIX, BRUTE_FORCE, GIVEN = range(5)
 GLOBAL_NONE, GLOBAL_TENSOR_AMAX, GLOBAL_USER, GLOBAL_SEARCH = range(4)
+COUNT_REPLICAS = 64          # FP4Q_COUNT_REPLICAS: rows of the fused code counts
 
 
 class Config(ctypes.Structure):
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
         L.fp4q_workspace_bytes.argtypes = [cp, i64, i64]
         L.fp4q_quantize.restype = ctypes.c_int
         L.fp4q_quantize.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, p, ctypes.c_int, i64, p, p, p]
+        L.fp4q_quantize_histogram.restype = ctypes.c_int
+        L.fp4q_quantize_histogram.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, p, ctypes.c_int, i64, p,
+                                              p, p, p]
         L.fp4q_quantize_noalloc.restype = ctypes.c_int
         L.fp4q_quantize_noalloc.argtypes = [cp, p, ctypes.c_int, i64, i64, i64, p, p, p, p, ctypes.c_int, i64, p, p]
         L.fp4q_dequantize.restype = ctypes.c_int
@@ -231,6 +235,28 @@ def fp4q_quantize(cfg, x, codes, scales, g=None, dequant=None, block_mse=None, w
     _check(st, "fp4q_quantize")
 
 
+def fp4q_quantize_histogram(cfg, x, codes, scales, counts, g=None, dequant=None, block_mse=None, workspace=None,
+                            stream=None):
+    """fp4q_quantize that also adds the written codes' occupancy to counts
+    (int64 [COUNT_REPLICAS, 16]; the occupancy is counts.sum(0))."""
+    rows, cols, ld = _rows_cols_ld(x)
+    nb = cols // cfg.block
+    _dense(codes, torch.uint8, (rows, cols // 2), "codes")
+    _dense(scales, torch.uint8, (rows, nb), "scales")
+    _dense(block_mse, torch.float32, (rows, nb), "block_mse")
+    _dense(counts, torch.int64, (COUNT_REPLICAS, 16), "counts")
+    _scalar_g(g)
+    _workspace_ok(workspace, cfg, rows, cols)
+    dq_dt, ld_dq = F32, cols
+    if dequant is not None:
+        ld_dq = _out_2d(dequant, rows, cols, "dequant")
+        dq_dt = dtype_code(dequant)
+    st = lib().fp4q_quantize_histogram(ctypes.byref(cfg), _ptr(x), dtype_code(x), rows, cols, ld, _ptr(codes),
+                                       _ptr(scales), _ptr(g), _ptr(dequant), dq_dt, ld_dq, _ptr(block_mse),
+                                       _ptr(counts), _ptr(workspace), _stream(stream))
+    _check(st, "fp4q_quantize_histogram")
+
+
 def fp4q_quantize_noalloc(cfg, x, codes, scales, g=None, dequant=None, block_mse=None, stream=None):
     """fp4q_quantize with the workspace in the library's static device scratch."""
     rows, cols, ld = _rows_cols_ld(x)
@@ -350,9 +376,12 @@ def _workspace(cfg, rows, cols, device):
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
 
 
-def quantize(x, cfg, dequant_dtype=None, want_mse=True, scales=None, stream=None):
+def quantize(x, cfg, dequant_dtype=None, want_mse=True, scales=None, counts=None, stream=None):
     """Quantize a 2-D device tensor; returns dict(codes, scales, g, dequant, mse).
-    With stream, the outputs are allocated on and the kernels run on it."""
+    counts: an int64 device tensor [COUNT_REPLICAS, 16] (counts_buffer())
+    to which the written codes' occupancy is added, fused into the quantize
+    kernels; occupancy(counts) sums its rows.  With stream, the outputs are
+    allocated on and the kernels run on it."""
     rows, cols, _ = _rows_cols_ld(x)
     dev = x.device
     with _on(stream):
@@ -362,7 +391,11 @@ def quantize(x, cfg, dequant_dtype=None, want_mse=True, scales=None, stream=None
         g = torch.empty(1, dtype=torch.float32, device=dev)
         dq = None if dequant_dtype is None else torch.empty((rows, cols), dtype=dequant_dtype, device=dev)
         mse = torch.empty((rows, cols // cfg.block), dtype=torch.float32, device=dev) if want_mse else None
-        fp4q_quantize(cfg, x, codes, scales, g, dq, mse, _workspace(cfg, rows, cols, dev), stream)
+        ws = _workspace(cfg, rows, cols, dev)
+        if counts is None:
+            fp4q_quantize(cfg, x, codes, scales, g, dq, mse, ws, stream)
+        else:
+            fp4q_quantize_histogram(cfg, x, codes, scales, counts, g, dq, mse, ws, stream)
     return dict(codes=codes, scales=scales, g=g, dequant=dq, mse=mse)
 
 
@@ -408,6 +441,16 @@ def relaxed_fakequant_bwd(w, scales, c, grad_out, cfg, sub_block=8, g=None, stre
         grad_c = torch.empty((rows, cols // sub_block), dtype=torch.float32, device=w.device)
         fp4q_relaxed_fakequant_bwd(cfg, w, scales, c, sub_block, grad_out, grad_c, g, stream)
     return grad_c
+
+
+def counts_buffer(device):
+    """A zeroed buffer for the fused code counts of quantize(counts=...)."""
+    return torch.zeros((COUNT_REPLICAS, 16), dtype=torch.int64, device=device)
+
+
+def occupancy(counts):
+    """The 16 code counts of a fused-count buffer (the sum of its rows)."""
+    return counts.sum(0)
 
 
 def code_histogram(codes, stream=None):

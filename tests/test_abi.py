@@ -117,6 +117,27 @@ def test_histogram_validation():
     assert L.fp4q_code_histogram(P(A), 4, 64, P(A + 4), None) == F.ERR_ALIGNMENT
 
 
+def quant_hist(cfg, counts=A, x=A, rows=16, cols=64, ld=64, codes=A, scales=A, g=A, ws=A):
+    return F.lib().fp4q_quantize_histogram(ctypes.byref(cfg) if cfg is not None else None, P(x), F.F32, rows,
+                                           cols, ld, P(codes), P(scales), P(g), None, F.F32, cols, None,
+                                           P(counts), P(ws), None)
+
+
+@needs_lib
+@cpu_only
+def test_quantize_histogram_validation():
+    """The quantize call with fused code counts: counts is required and
+    8-byte aligned; the rest is checked as for fp4q_quantize."""
+    nv = F.nvfp4()
+    assert quant_hist(None) == F.ERR_INVALID_ARG
+    assert quant_hist(nv, counts=0) == F.ERR_INVALID_ARG
+    assert quant_hist(nv, counts=A + 4) == F.ERR_ALIGNMENT
+    assert quant_hist(nv, codes=0) == F.ERR_INVALID_ARG
+    assert quant_hist(F.config(1, 12)) == F.ERR_SHAPE
+    assert quant_hist(nv, x=A + 4) == F.ERR_ALIGNMENT
+    assert quant_hist(nv, ws=0) == F.ERR_INVALID_ARG                 # TENSOR_AMAX needs the workspace
+
+
 @needs_lib
 @cpu_only
 def test_gemm_validation_and_workspace():

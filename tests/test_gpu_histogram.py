@@ -1,7 +1,9 @@
 """GPU parity of the codebook-occupancy histogram (TORQ page, section 2.B)
 against the oracle: exact integer counts on random bytes with ragged sizes,
 an empty tensor, and the codes the library itself produces on the 4096 x
-4096 workload (including the collapse onto the zero codes at 1e-4)."""
+4096 workload (including the collapse onto the zero codes at 1e-4); then the
+counts fused into the quantize kernels, streaming and brute force, against
+the oracle's histogram of the oracle's codes."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,7 @@ from microscaling_fp4_block_fp4q_amd import fp4q as F
 from microscaling_fp4_block_fp4q_amd import synth as S
 from oracle import oracle as O
 
-from gpu_helpers import DEV, note
+from gpu_helpers import DEV, assert_same, note, oracle_quantize
 
 pytestmark = pytest.mark.gpu
 
@@ -37,3 +39,95 @@ def test_codes_of_the_workload(O_lib, kind):
     assert int(want.sum()) == x.size
     if kind == "normal_1e-4":
         assert int(want[0] + want[8]) == x.size          # every E4M3 scale underflows without g
+
+
+# --------------------------------------------------------------------------
+# occupancy counted inside the quantize kernels (fp4q_quantize_histogram)
+# --------------------------------------------------------------------------
+
+# bit patterns of NaN, -inf, +0, -0 per input type (bf16 / fp16 arrays hold bits)
+_SPECIAL_BITS = {S.BF16: (0x7FC0, 0xFF80, 0x0000, 0x8000), S.F16: (0x7E00, 0xFC00, 0x0000, 0x8000)}
+
+
+def _special(x: np.ndarray, dt: int) -> np.ndarray:
+    """NaN / inf / signed zeros in a few blocks (NaN blocks write sign-only codes)."""
+    y = x.copy()
+    flat = y.reshape(-1)
+    nan, ninf, pz, nz = (np.nan, -np.inf, 0.0, -0.0) if dt == S.F32 else _SPECIAL_BITS[dt]
+    flat[5] = nan
+    flat[70] = ninf
+    flat[200:216] = pz
+    flat[216:232] = nz
+    return y
+
+
+FUSED = [
+    # (what, cfg, dtype, rows, cols)
+    ("nvfp4 amax f32", F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_TENSOR_AMAX), S.F32, 37, 4096),
+    ("mxfp4 H32 bf16", F.config(F.E8M0, 32, F.ABSMAX, F.GLOBAL_NONE, hadamard=32), S.BF16, 29, 2048),
+    ("4o6 H16 bf16", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_TENSOR_AMAX, hadamard=16), S.BF16, 33, 1024),
+    ("prevent-zero B8 f16", F.config(F.E4M3, 8, F.PREVENT_ZERO, F.GLOBAL_NONE), S.F16, 19, 520),
+    ("ue5m3 B32 f32", F.config(F.UE5M3, 32, F.ABSMAX, F.GLOBAL_NONE), S.F32, 7, 96),
+    ("brute B4 f32", F.config(F.E4M3, 4, F.BRUTE_FORCE, F.GLOBAL_TENSOR_AMAX), S.F32, 21, 1028),
+    ("brute B8 f16 H16", F.config(F.E4M3, 8, F.BRUTE_FORCE, F.GLOBAL_NONE, hadamard=16), S.F16, 9, 512),
+    ("brute B32 e8m0 bf16", F.config(F.E8M0, 32, F.BRUTE_FORCE, F.GLOBAL_NONE), S.BF16, 11, 2048),
+]
+
+
+@pytest.mark.parametrize("what,cfg,dt,rows,cols", FUSED, ids=[f[0] for f in FUSED])
+@pytest.mark.parametrize("special", [False, True], ids=["finite", "nan-inf"])
+def test_fused_counts_match_oracle(O_lib, what, cfg, dt, rows, cols, special):
+    """Codes equal the oracle's, and the fused counts equal the oracle's
+    histogram of those codes; a second call adds the same counts again."""
+    x = S.normal(rows, cols, seed=rows * cols + cfg.strategy, dt=dt)
+    if special:
+        x = _special(x, dt)
+    ref = oracle_quantize(x, dt, cfg)
+    want = O.code_histogram(ref["codes"])
+    note(f"fused counts {what} {rows}x{cols} special={special}")
+    xt = S.to_torch(x, dt, DEV)
+    counts = F.counts_buffer(DEV)
+    r = F.quantize(xt, cfg, want_mse=False, counts=counts)
+    torch.cuda.synchronize()
+    assert_same(S.from_torch(r["codes"]), ref["codes"], "codes")
+    assert np.array_equal(F.occupancy(counts).cpu().numpy().astype(np.uint64), want)
+    assert int(want.sum()) == rows * cols
+    assert int(counts.min()) >= 0
+    F.quantize(xt, cfg, want_mse=False, counts=counts)
+    torch.cuda.synchronize()
+    assert np.array_equal(F.occupancy(counts).cpu().numpy().astype(np.uint64), 2 * want)
+
+
+def test_fused_counts_given_scales(O_lib):
+    """GIVEN strategy: the codes come from the caller's scales."""
+    rows, cols = 23, 768
+    cfg_pick = F.config(F.E4M3, 16, F.ABSMAX, F.GLOBAL_USER, global_scale=0.0078125)
+    x = S.normal(rows, cols, seed=91, dt=S.F32)
+    sc = oracle_quantize(x, S.F32, cfg_pick)["scales"]
+    cfg = F.config(F.E4M3, 16, F.GIVEN, F.GLOBAL_USER, global_scale=0.0078125)
+    ref = oracle_quantize(x, S.F32, cfg, scales_in=sc)
+    note("fused counts given scales 23x768")
+    counts = F.counts_buffer(DEV)
+    r = F.quantize(S.to_torch(x, S.F32, DEV), cfg, want_mse=False,
+                   scales=torch.from_numpy(np.ascontiguousarray(sc)).to(DEV), counts=counts)
+    torch.cuda.synchronize()
+    assert_same(S.from_torch(r["codes"]), ref["codes"], "codes")
+    assert np.array_equal(F.occupancy(counts).cpu().numpy().astype(np.uint64), O.code_histogram(ref["codes"]))
+
+
+@pytest.mark.parametrize("kind", ["normal", "normal_1e-4"])
+@pytest.mark.parametrize("strategy", [F.ABSMAX, F.FOUR_OVER_SIX, F.BRUTE_FORCE])
+def test_fused_counts_full_size(O_lib, kind, strategy):
+    """On the 4096 x 4096 workload (grid capped at the resident workgroups,
+    every workgroup adding its totals) the fused counts equal the oracle's
+    histogram of the codes written in the same call."""
+    x = S.config2()[kind]
+    cfg = F.config(F.E4M3, 16 if strategy != F.BRUTE_FORCE else 4, strategy, F.GLOBAL_TENSOR_AMAX)
+    note(f"fused counts full size {kind} strategy={strategy}")
+    counts = F.counts_buffer(DEV)
+    r = F.quantize(S.to_torch(x, S.F32, DEV), cfg, want_mse=False, counts=counts)
+    torch.cuda.synchronize()
+    want = O.code_histogram(r["codes"].cpu().numpy())
+    assert np.array_equal(F.occupancy(counts).cpu().numpy().astype(np.uint64), want)
+    assert int((counts.sum(1) > 0).sum()) == F.COUNT_REPLICAS      # the resident grid uses every row
+    assert int(want.sum()) == x.size
