@@ -902,10 +902,14 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 template <int U, int B>
 struct BfWaveLds {
     static constexpr int NBLK = kTileUnits * (U / B);
+    static constexpr int NMASK = B == 4 ? NBLK : 1;   // candidate masks (bf_search_tile_mask)
     char tile[kTileUnits * slot_bytes<U>()];
     unsigned long long best[NBLK];
     uint32_t start[NBLK + 1];
     uint8_t clo[NBLK];
+    unsigned long long mask[NMASK];
+    uint8_t mbase[NMASK];
+    uint8_t movf[NMASK];
 };
 
 // Brute-force search of one tile (exhaustive argmin, computed as branch and
@@ -1044,6 +1048,298 @@ __device__ __forceinline__ void bf_search_tile(const float (&y)[U], bool active,
     wave_sync_lds();
 }
 
+// ---------------------------------------------------------------------------
+// Brute force for blocks of 4 with E4M3 scales in the division-free range:
+// candidate masks instead of the window.  Each element's squared error is
+// one term of the block's tree sum, and a tree sum of non-negative terms is
+// at least each term, so a code c can only reach SSE_c <= tau (tau = the
+// best start SSE) if every element's own error e_i(c) <= tau.  For an
+// element a the computed error (a - fl(r S))^2 with r on the E2M1 grid is at
+// most tau only if |a - r S| <= delta, delta = sqrt(tau) plus the rounding
+// of the product, difference and square, for some grid value r in {6, 4,
+// 3, 2, 1.5, 1, 0.5} (r = 0 needs a <= delta).  So the admissible scales of
+// a are the union of the intervals S in [(a - delta) / r, (a + delta) / r]:
+// in E4M3 codes of S / g, the r = 6 interval and its doublings (r = 3, 1.5)
+// and the r = 4 interval and its doublings (r = 2, 1, 0.5), where doubling a
+// value adds 8 to a normal code (and about doubles a subnormal one; those
+// bounds are widened by a code).  The candidates of a block are the codes
+// admissible for both its largest and its second largest element, minus the
+// two start codes already evaluated; every other code has SSE > tau and
+// cannot win.  Masks are 64 codes wide from the lowest admissible code of
+// the largest element; codes of its intervals above that frame (possible
+// only for a very large tau) are all kept as candidates.
+// ---------------------------------------------------------------------------
+
+// E4M3 codes of a scale value u (in units of g) in the normal range (u >=
+// 2^-6, code 8 up): the smallest code with a value >= u and the largest
+// with a value <= u, from the fp32 bits ((e + 7) << 3 | top mantissa bits).
+// Below 2^-6 they return 0 and 8, bounds that contain every subnormal code;
+// far above 448 or for an infinite u they return codes past 126.
+__device__ __forceinline__ int e4m3_code_ceil(float u) {
+    return u < 0x1p-6f ? 0 : (int)((as_u(u) + 0xFFFFFu) >> 20) - 960;
+}
+__device__ __forceinline__ int e4m3_code_floor(float u) {
+    return u < 0x1p-6f ? 8 : (int)(as_u(u) >> 20) - 960;
+}
+
+// The same with the subnormal codes m 2^-9 (m = 1..7) resolved.
+__device__ __forceinline__ int e4m3_code_ceil_sub(float u) {
+    if (u >= 0x1p-6f) return e4m3_code_ceil(u);
+    return u > 0.0f ? (int)__builtin_ceilf(u * 512.0f) : 0;
+}
+__device__ __forceinline__ int e4m3_code_floor_sub(float u) {
+    if (u >= 0x1p-6f) return e4m3_code_floor(u);
+    return u > 0.0f ? (int)(u * 512.0f) : -1;
+}
+
+// A bound on the code of twice a code's value: + 8 for normal codes; below
+// code 8 (value m 2^-9) twice the value is code 2m, so the bounds widen by
+// one code to stay on the safe side.
+__device__ __forceinline__ int doubled_lo(int l) { return min(2 * l - 1, l + 8); }
+__device__ __forceinline__ int doubled_hi(int h) { return min(2 * h + 1, h + 8); }
+
+// Bits 0 .. w (nothing for w < 0, all for w >= 63).
+__device__ __forceinline__ unsigned long long low_bits(int w) {
+    return w < 0 ? 0ull : (~0ull >> (63 - (w < 63 ? w : 63)));
+}
+
+// Bits [l - base, h - base] of a 64-code frame (nothing when empty).
+__device__ __forceinline__ unsigned long long frame_bits(int l, int h, int base) {
+    int lo = l - base, hi = h - base;
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > 63 ? 63 : hi;
+    return lo <= hi ? ((~0ull >> (63 - (hi - lo))) << lo) : 0ull;
+}
+
+// Admissible codes of one element a, as a pattern relative to its lowest
+// admissible code l6 (the r = 6 bound): the r = 6 and r = 4 intervals and
+// their doublings, 8 codes apart.  inv6 / inv4 are fl(1 / fl(6 g)) and
+// fl(1 / fl(4 g)) times (1 -+ 2^-18) for the lower / upper bounds (margin
+// for the rounding of the bounds themselves).  When the r = 6 interval
+// reaches below code 8 the doubling is not a shift by 8: then every code
+// between the lowest and the highest bound is kept.  top receives the
+// highest admissible code (the r = 0.5 end), and sat is set when admissible
+// codes may lie past bit 63 of the pattern.
+__device__ __forceinline__ unsigned long long element_pattern(float a, float delta, float inv6_lo, float inv6_hi,
+                                                              float inv4_lo, float inv4_hi, int& l6, int& top,
+                                                              bool& sat) {
+    const float lo = a - delta, hi = a + delta;
+    l6 = e4m3_code_ceil(lo * inv6_lo);
+    const int h6 = e4m3_code_floor(hi * inv6_hi);
+    const int l4 = e4m3_code_ceil(lo * inv4_lo);
+    const int h4 = e4m3_code_floor(hi * inv4_hi);
+    const unsigned long long p6 = low_bits(h6 - l6);
+    const int d46 = l4 - l6;                                        // 4 to 6 for normal codes (ratio 1.5)
+    const unsigned long long p4 = low_bits(h4 - l4) << (d46 < 63 ? d46 : 63);
+    const unsigned long long q = p6 | p4;
+    unsigned long long pat = q | (q << 8) | (q << 16) | (p4 << 24);
+    top = h4 + 24;
+    if (l6 < 8) {
+        // subnormal codes involved (rare, and a few codes only): every code
+        // from the r = 6 lower bound to the r = 0.5 upper bound
+        l6 = e4m3_code_ceil_sub(lo * inv6_lo);
+        top = doubled_hi(doubled_hi(doubled_hi(e4m3_code_floor_sub(hi * inv4_hi))));
+        pat = low_bits(top - l6);
+    }
+    sat = top - l6 > 63;
+    return pat;
+}
+
+template <int U>
+__device__ __forceinline__ void bf_search_tile_mask(const float (&y)[U], bool active, float g, float inv_six_g,
+                                                    float inv_four_g, const BfTable& s_bf, BfWaveLds<U, 4>& W,
+                                                    int lane, bool (&nan_blk)[U / 4]) {
+    constexpr int B = 4;
+    constexpr int NB = U / B;
+    constexpr int SLOT = slot_bytes<U>();
+    constexpr int NBLK = kTileUnits * NB;
+    constexpr int TOP = (int)scale_top<SF_E4M3>();
+    const float inv6_lo = inv_six_g * (1.0f - 0x1p-18f), inv6_hi = inv_six_g * (1.0f + 0x1p-18f);
+    const float inv4_lo = inv_four_g * (1.0f - 0x1p-18f), inv4_hi = inv_four_g * (1.0f + 0x1p-18f);
+
+#pragma unroll
+    for (int i = 0; i < U / 4; ++i)
+        reinterpret_cast<float4*>(W.tile + lane * SLOT)[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+
+    uint32_t n[NB];
+    static_for<NB>([&](auto bi) {
+        constexpr int b = decltype(bi)::value;
+        uint32_t m0 = as_u(y[b * B]) & 0x7FFFFFFFu, m1 = as_u(y[b * B + 1]) & 0x7FFFFFFFu;
+        uint32_t m2 = as_u(y[b * B + 2]) & 0x7FFFFFFFu, m3 = as_u(y[b * B + 3]) & 0x7FFFFFFFu;
+        const uint32_t hi01 = max(m0, m1), lo01 = min(m0, m1), hi23 = max(m2, m3), lo23 = min(m2, m3);
+        const uint32_t ab = max(hi01, hi23);
+        const uint32_t a2b = max(min(hi01, hi23), max(lo01, lo23));    // second largest magnitude
+        nan_blk[b] = ab >= 0x7F800000u || !(g < __builtin_inff());
+        n[b] = 0;
+        unsigned long long best = ~0ull, mask = 0ull;
+        int base = 0, ovf = 0;
+        if (!nan_blk[b] && active) {
+            const float a_b = as_f(ab);
+            if (a_b <= s_bf.t0[1]) {
+                best = pack_candidate(0.0f, 1u);        // every element encodes to 0 at every code: all tie
+            } else {
+                const uint32_t s6 = scale_encode<SF_E4M3>(a_b * inv_six_g), s4 = scale_encode<SF_E4M3>(a_b * inv_four_g);
+                const uint32_t c1 = s6 > 0u ? s6 : 1u, c2 = s4 > 0u ? s4 : 1u;
+                float rc[B];
+                const float2 e1 = s_bf.sr[c1], e2 = s_bf.sr[c2];
+                best = pack_candidate(encode_block<SF_E4M3, B, b * B, false, true>(y, e1.x, e1.y, rc), c1);
+                if (c2 != c1) {
+                    const unsigned long long b2 =
+                        pack_candidate(encode_block<SF_E4M3, B, b * B, false, true>(y, e2.x, e2.y, rc), c2);
+                    best = b2 < best ? b2 : best;
+                }
+                const float tau = as_f((uint32_t)(best >> 32));
+                // sqrt with a relative margin far above its error, the
+                // rounding of product, difference and square (relative to
+                // a), and the square's underflow
+                const float delta = __builtin_amdgcn_sqrtf(tau) * (1.0f + 0x1p-16f) + a_b * 0x1p-20f + 0x1p-70f;
+                if (tau < __builtin_inff() && a_b > delta) {
+                    int top, l2, top2;
+                    bool sat1, sat2;
+                    mask = element_pattern(a_b, delta, inv6_lo, inv6_hi, inv4_lo, inv4_hi, base, top, sat1);
+                    // the second element, placed in the frame of the first;
+                    // moved down, the vacated top bits are kept when its
+                    // pattern may continue past bit 63
+                    const float a2 = as_f(a2b);
+                    const unsigned long long p2 =
+                        element_pattern(a2, delta, inv6_lo, inv6_hi, inv4_lo, inv4_hi, l2, top2, sat2);
+                    const int sh = l2 - base;
+                    unsigned long long m2;
+                    if (sh >= 0) {
+                        m2 = sh < 64 ? p2 << sh : 0ull;
+                    } else {
+                        m2 = sh > -64 ? p2 >> -sh : 0ull;
+                        if (sat2) m2 |= sh > -64 ? ~0ull << (64 + sh) : ~0ull;
+                    }
+                    mask &= a2 > delta ? m2 : ~0ull;
+                    // codes 1 .. TOP only, and not the two starts
+                    if (base == 0) mask &= ~1ull;
+                    if (base + 63 > TOP) mask = base <= TOP ? mask & (~0ull >> (base + 63 - TOP)) : 0ull;
+                    const int d1 = (int)c1 - base, d2 = (int)c2 - base;
+                    if (d1 >= 0 && d1 <= 63) mask &= ~(1ull << d1);
+                    if (d2 >= 0 && d2 <= 63) mask &= ~(1ull << d2);
+                    top = top < TOP ? top : TOP;
+                    ovf = top - (base + 63) > 0 ? top - (base + 63) : 0;
+                } else {
+                    // The largest element may encode to zero within tau (or
+                    // tau is infinite).  From the first code at which every
+                    // element encodes to zero (S >= 4 a_b is enough) all
+                    // larger codes tie with it, so the candidates are the
+                    // codes from 1 up to a bound on that code.
+                    int up = TOP;
+                    if (tau < __builtin_inff()) {
+                        up = e4m3_code_ceil_sub(a_b * inv_four_g * 16.0f * (1.0f + 0x1p-18f));
+                        up = up < TOP ? up : TOP;
+                    }
+                    base = 1;
+                    mask = frame_bits(1, up, 1);
+                    const int d1 = (int)c1 - 1, d2 = (int)c2 - 1;
+                    if (d1 <= 63) mask &= ~(1ull << d1);
+                    if (d2 <= 63) mask &= ~(1ull << d2);
+                    ovf = up - 64 > 0 ? up - 64 : 0;
+                }
+                n[b] = (uint32_t)__popcll(mask) + (uint32_t)ovf;
+            }
+        }
+        W.best[lane * NB + b] = best;
+        W.mask[lane * NB + b] = mask;
+        W.mbase[lane * NB + b] = (uint8_t)base;
+        W.movf[lane * NB + b] = (uint8_t)ovf;
+    });
+
+    uint32_t mine = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mine += n[b];
+    const uint32_t incl = wave_inclusive_sum(mine, lane);
+    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+    uint32_t run = incl - mine;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        W.start[lane * NB + b] = run;
+        run += n[b];
+    }
+    if (lane == 63) W.start[NBLK] = total;
+    wave_sync_lds();
+
+    const uint32_t j0 = (uint32_t)(((uint64_t)total * lane) >> 6);
+    const uint32_t j1 = (uint32_t)(((uint64_t)total * (lane + 1)) >> 6);
+    if (j0 < j1) {
+        uint32_t lo = 0, hi = NBLK;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if (W.start[mid] <= j0) lo = mid; else hi = mid - 1;
+        }
+        // cursor over the candidates: block k (values yk, mask m from bit
+        // base, then ovf codes from base + 64), survivor index range k_end
+        uint32_t k = lo;
+        float yk[B];
+        unsigned long long m;
+        int base, ovf_pos;
+        auto load_block = [&](uint32_t kk) {
+            const float4 v = *reinterpret_cast<const float4*>(W.tile + (kk / NB) * SLOT + (kk % NB) * B * 4);
+            yk[0] = v.x; yk[1] = v.y; yk[2] = v.z; yk[3] = v.w;
+            m = W.mask[kk];
+            base = W.mbase[kk];
+            ovf_pos = 0;
+        };
+        load_block(k);
+        uint32_t k_end = W.start[k + 1];
+        {
+            // skip the candidates of block k before j0
+            uint32_t t = j0 - W.start[k];
+            const uint32_t pc = (uint32_t)__popcll(m);
+            if (t >= pc) {
+                ovf_pos = (int)(t - pc);
+                m = 0ull;
+            } else {
+#pragma unroll 1
+                for (; t > 0; --t) m &= m - 1ull;
+            }
+        }
+        // candidate j: its block, code and values
+        auto next = [&](uint32_t j, uint32_t& kk, uint32_t& c, float (&v)[B]) {
+            while (j >= k_end) {
+                ++k;
+                k_end = W.start[k + 1];
+                if (j < k_end) load_block(k);
+            }
+            if (m) {
+                c = (uint32_t)(base + __builtin_ctzll(m));
+                m &= m - 1ull;
+            } else {
+                c = (uint32_t)(base + 64 + ovf_pos);
+                ++ovf_pos;
+            }
+            kk = k;
+#pragma unroll
+            for (int i = 0; i < B; ++i) v[i] = yk[i];
+        };
+        // two independent candidates per step (the second repeats the first
+        // at an odd end)
+#pragma unroll 1
+        for (uint32_t j = j0; j < j1; j += 2) {
+            uint32_t ka, ca, kb, cb;
+            float va[B], vb[B];
+            next(j, ka, ca, va);
+            const bool two = j + 1 < j1;
+            if (two) {
+                next(j + 1, kb, cb, vb);
+            } else {
+                kb = ka; cb = ca;
+#pragma unroll
+                for (int i = 0; i < B; ++i) vb[i] = va[i];
+            }
+            const float2 ea = s_bf.sr[ca], eb = s_bf.sr[cb];
+            float ra[B], rb[B];
+            const float sa = encode_block<SF_E4M3, B, 0, false, true>(va, ea.x, ea.y, ra);
+            const float sb = encode_block<SF_E4M3, B, 0, false, true>(vb, eb.x, eb.y, rb);
+            atomicMin(&W.best[ka], pack_candidate(sa, ca));
+            atomicMin(&W.best[kb], pack_candidate(sb, cb));
+        }
+    }
+    wave_sync_lds();
+}
+
 // SSE of block BI of a unit at the winning code c of a brute-force search,
 // computed as the quantizer computes it (r receives the grid values).
 template <int SF, int B, int BI, int U>
@@ -1149,8 +1445,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
         }
         bool nan_blk[NB];
-        if (fast) bf_search_tile<SF, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
-        else bf_search_tile<SF, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+        if constexpr (B == 4 && SF == SF_E4M3) {
+            if (fast) bf_search_tile_mask<U>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            else bf_search_tile<SF, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+        } else {
+            if (fast) bf_search_tile<SF, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            else bf_search_tile<SF, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+        }
 
         // encode every block at its winning code
         uint32_t cw[code_words(U)];
@@ -1230,8 +1531,13 @@ __global__ __launch_bounds__(kThreads) void k_gsearch_bf(GSearchArgs p) {
             float y[U];
             bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
             bool nan_blk[NB];
-            if (fast) bf_search_tile<SF_E4M3, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
-            else bf_search_tile<SF_E4M3, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            if constexpr (B == 4) {
+                if (fast) bf_search_tile_mask<U>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+                else bf_search_tile<SF_E4M3, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            } else {
+                if (fast) bf_search_tile<SF_E4M3, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+                else bf_search_tile<SF_E4M3, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            }
             double e[NB];
             static_for<NB>([&](auto bi) {
                 constexpr int b = decltype(bi)::value;
