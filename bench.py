@@ -680,7 +680,39 @@ def time_histogram(F, torch, x, reps=10):
     return {"ms": round(ms, 4), "GB/s": round(R * C / 2 / (ms * 1e6), 1),
             "zero_code_fraction": round(float(h[0] + h[8]) / (R * C), 4),
             "what": "not part of the step: counts of the 16 nibble codes of the NVFP4 (block 16, no per-tensor "
-                    "scale) codes of the 4096x4096 N(0,1) input, 8 MiB of code bytes"}
+                    "scale) codes of the 4096x4096 N(0,1) input, 8 MiB of code bytes (stand-alone pass)",
+            "fused": time_fused_counts(F, torch, x)}
+
+
+def time_fused_counts(F, torch, x, reps=20, rounds=3):
+    """Cost of counting the code occupancy inside the quantize kernels
+    (fp4q_quantize_histogram) against the same quantize call without it, on
+    one 4096 x 4096 fp32 input: best of `rounds` interleaved means."""
+    R, C = x.shape
+    dev = x.device
+    out = {}
+    for name, cfg in (("mxfp4 abs-max", F.mxfp4()),
+                      ("nvfp4 4-over-6 tensor-amax", F.config(F.E4M3, 16, F.FOUR_OVER_SIX, F.GLOBAL_TENSOR_AMAX)),
+                      ("brute-force block 4", F.config(F.E4M3, 4, F.BRUTE_FORCE, F.GLOBAL_NONE))):
+        codes = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((R, C // cfg.block), dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+        n = F.workspace_bytes(cfg, R, C)
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev) if n else None
+        counts = F.counts_buffer(dev)
+        plain = lambda: F.fp4q_quantize(cfg, x, codes, scales, g, None, None, ws)
+        counted = lambda: F.fp4q_quantize_histogram(cfg, x, codes, scales, counts, g, None, None, ws)
+        r = 5 if cfg.strategy == F.BRUTE_FORCE else reps
+        tp, tc = [], []
+        for _ in range(rounds):
+            tp.append(time_fn(torch, plain, r))
+            tc.append(time_fn(torch, counted, r))
+        p_ms, c_ms = min(tp), min(tc)
+        out[name] = {"ms": round(p_ms, 4), "ms_with_counts": round(c_ms, 4), "overhead": round(c_ms / p_ms - 1, 4)}
+    out["what"] = ("the same quantize call (codes + scales) with and without the fused 16-code occupancy count "
+                   "(fp4q_quantize_histogram: per-thread counters, one atomic per code per workgroup into 64 "
+                   "replica rows)")
+    return out
 
 
 MFMA_FP4_PEAK_TFLOPS = 10100.0              # MI355X dense FP4 matrix peak, published
@@ -830,7 +862,7 @@ def bf_roofline(calls, per_call, dom, B, valu_probe):
     VALU lane-instructions (SQ_INSTS_VALU x 64 per dispatch, from the
     committed counter profile of the same calls on the same sources) over
     the live mean launch time, against the fp32 vector peak."""
-    kname = f"k_quant_bf<float, {B}, 0, 1>"
+    kname = f"k_quant_bf<float, {B}, 0, 1, false>"
     prof = load_profile("counters_bench_dominant")
     kc = kernel_counters(prof, kname)
     solo = [(c, ms) for c, ms in dom if c.meta.get("global_mode") == "none"]
