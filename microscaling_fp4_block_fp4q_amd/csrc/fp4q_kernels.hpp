@@ -902,7 +902,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 template <int U, int B>
 struct BfWaveLds {
     static constexpr int NBLK = kTileUnits * (U / B);
-    static constexpr int NMASK = B == 4 ? NBLK : 1;   // candidate masks (bf_search_tile_mask)
+    static constexpr int NMASK = B <= 8 ? NBLK : 1;   // candidate masks (bf_search_tile_mask)
     char tile[kTileUnits * slot_bytes<U>()];
     unsigned long long best[NBLK];
     uint32_t start[NBLK + 1];
@@ -1145,11 +1145,25 @@ __device__ __forceinline__ unsigned long long element_pattern(float a, float del
     return pat;
 }
 
-template <int U>
+// A pattern of codes relative to code l (bit i = code l + i) moved into the
+// frame from base; when sat, the pattern may continue past its bit 63 and
+// the frame bits it would reach are kept.
+__device__ __forceinline__ unsigned long long place_pattern(unsigned long long pat, int l, bool sat, int base) {
+    const int sh = l - base;
+    if (sh >= 0) return sh < 64 ? pat << sh : 0ull;
+    unsigned long long m = sh > -64 ? pat >> -sh : 0ull;
+    if (sat) m |= sh > -64 ? ~0ull << (64 + sh) : ~0ull;
+    return m;
+}
+
+// Blocks of 4: the masks alone (no window).  Blocks of 8: the window of
+// bf_window (its bounds on the zero bin and the saturated maximum cut what
+// two elements cannot) intersected with the masks.
+template <int U, int B>
 __device__ __forceinline__ void bf_search_tile_mask(const float (&y)[U], bool active, float g, float inv_six_g,
-                                                    float inv_four_g, const BfTable& s_bf, BfWaveLds<U, 4>& W,
-                                                    int lane, bool (&nan_blk)[U / 4]) {
-    constexpr int B = 4;
+                                                    float inv_four_g, const BfTable& s_bf, BfWaveLds<U, B>& W,
+                                                    int lane, bool (&nan_blk)[U / B]) {
+    static_assert(B == 4 || B == 8, "candidate masks for blocks of 4 and 8");
     constexpr int NB = U / B;
     constexpr int SLOT = slot_bytes<U>();
     constexpr int NBLK = kTileUnits * NB;
@@ -1164,80 +1178,100 @@ __device__ __forceinline__ void bf_search_tile_mask(const float (&y)[U], bool ac
     uint32_t n[NB];
     static_for<NB>([&](auto bi) {
         constexpr int b = decltype(bi)::value;
-        uint32_t m0 = as_u(y[b * B]) & 0x7FFFFFFFu, m1 = as_u(y[b * B + 1]) & 0x7FFFFFFFu;
-        uint32_t m2 = as_u(y[b * B + 2]) & 0x7FFFFFFFu, m3 = as_u(y[b * B + 3]) & 0x7FFFFFFFu;
-        const uint32_t hi01 = max(m0, m1), lo01 = min(m0, m1), hi23 = max(m2, m3), lo23 = min(m2, m3);
-        const uint32_t ab = max(hi01, hi23);
-        const uint32_t a2b = max(min(hi01, hi23), max(lo01, lo23));    // second largest magnitude
+        // largest and second largest magnitude (integer compare of |y| bits)
+        uint32_t ab = 0, a2b = 0;
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const uint32_t v = as_u(y[b * B + i]) & 0x7FFFFFFFu;
+            a2b = max(a2b, min(ab, v));
+            ab = max(ab, v);
+        }
         nan_blk[b] = ab >= 0x7F800000u || !(g < __builtin_inff());
         n[b] = 0;
         unsigned long long best = ~0ull, mask = 0ull;
         int base = 0, ovf = 0;
         if (!nan_blk[b] && active) {
             const float a_b = as_f(ab);
-            if (a_b <= s_bf.t0[1]) {
-                best = pack_candidate(0.0f, 1u);        // every element encodes to 0 at every code: all tie
-            } else {
-                const uint32_t s6 = scale_encode<SF_E4M3>(a_b * inv_six_g), s4 = scale_encode<SF_E4M3>(a_b * inv_four_g);
-                const uint32_t c1 = s6 > 0u ? s6 : 1u, c2 = s4 > 0u ? s4 : 1u;
-                float rc[B];
-                const float2 e1 = s_bf.sr[c1], e2 = s_bf.sr[c2];
-                best = pack_candidate(encode_block<SF_E4M3, B, b * B, false, true>(y, e1.x, e1.y, rc), c1);
-                if (c2 != c1) {
-                    const unsigned long long b2 =
-                        pack_candidate(encode_block<SF_E4M3, B, b * B, false, true>(y, e2.x, e2.y, rc), c2);
-                    best = b2 < best ? b2 : best;
+            const uint32_t s6 = scale_encode<SF_E4M3>(a_b * inv_six_g), s4 = scale_encode<SF_E4M3>(a_b * inv_four_g);
+            const uint32_t c1 = s6 > 0u ? s6 : 1u, c2 = s4 > 0u ? s4 : 1u;
+            int wlo = 1, whi = TOP;                  // candidate codes [wlo, whi]
+            bool none = false;
+            if constexpr (B == 4) {
+                if (a_b <= s_bf.t0[1]) {
+                    best = pack_candidate(0.0f, 1u);    // every element encodes to 0 at every code: all tie
+                    none = true;
+                } else {
+                    float rc[B];
+                    const float2 e1 = s_bf.sr[c1], e2 = s_bf.sr[c2];
+                    best = pack_candidate(encode_block<SF_E4M3, B, b * B, false, true>(y, e1.x, e1.y, rc), c1);
+                    if (c2 != c1) {
+                        const unsigned long long b2 =
+                            pack_candidate(encode_block<SF_E4M3, B, b * B, false, true>(y, e2.x, e2.y, rc), c2);
+                        best = b2 < best ? b2 : best;
+                    }
                 }
+            } else {
+                uint32_t lo, hi;
+                best = bf_window<SF_E4M3, B, b * B, true>(y, a_b, c1, c2, s_bf, lo, hi);
+                wlo = (int)lo;
+                whi = (int)hi - 1;
+                none = hi <= lo;
+            }
+            if (!none) {
                 const float tau = as_f((uint32_t)(best >> 32));
                 // sqrt with a relative margin far above its error, the
                 // rounding of product, difference and square (relative to
                 // a), and the square's underflow
                 const float delta = __builtin_amdgcn_sqrtf(tau) * (1.0f + 0x1p-16f) + a_b * 0x1p-20f + 0x1p-70f;
-                if (tau < __builtin_inff() && a_b > delta) {
-                    int top, l2, top2;
+                int top;
+                if (B == 8 && whi - wlo < 7) {
+                    // a short window: masks would cost more than the evaluations they save
+                    base = wlo;
+                    mask = ~0ull;
+                    top = whi;
+                } else if (tau < __builtin_inff() && a_b > delta) {
+                    int l1, l2, top2;
                     bool sat1, sat2;
-                    mask = element_pattern(a_b, delta, inv6_lo, inv6_hi, inv4_lo, inv4_hi, base, top, sat1);
-                    // the second element, placed in the frame of the first;
-                    // moved down, the vacated top bits are kept when its
-                    // pattern may continue past bit 63
+                    const unsigned long long p1 =
+                        element_pattern(a_b, delta, inv6_lo, inv6_hi, inv4_lo, inv4_hi, l1, top, sat1);
                     const float a2 = as_f(a2b);
                     const unsigned long long p2 =
                         element_pattern(a2, delta, inv6_lo, inv6_hi, inv4_lo, inv4_hi, l2, top2, sat2);
-                    const int sh = l2 - base;
-                    unsigned long long m2;
-                    if (sh >= 0) {
-                        m2 = sh < 64 ? p2 << sh : 0ull;
+                    // frame from the largest element's lowest admissible
+                    // code (blocks of 4) or from the window's start
+                    if constexpr (B == 4) {
+                        base = l1;
+                        mask = p1;
                     } else {
-                        m2 = sh > -64 ? p2 >> -sh : 0ull;
-                        if (sat2) m2 |= sh > -64 ? ~0ull << (64 + sh) : ~0ull;
+                        base = wlo > l1 ? wlo : l1;
+                        mask = place_pattern(p1, l1, sat1, base);
                     }
-                    mask &= a2 > delta ? m2 : ~0ull;
-                    // codes 1 .. TOP only, and not the two starts
-                    if (base == 0) mask &= ~1ull;
-                    if (base + 63 > TOP) mask = base <= TOP ? mask & (~0ull >> (base + 63 - TOP)) : 0ull;
-                    const int d1 = (int)c1 - base, d2 = (int)c2 - base;
-                    if (d1 >= 0 && d1 <= 63) mask &= ~(1ull << d1);
-                    if (d2 >= 0 && d2 <= 63) mask &= ~(1ull << d2);
-                    top = top < TOP ? top : TOP;
-                    ovf = top - (base + 63) > 0 ? top - (base + 63) : 0;
+                    mask &= a2 > delta ? place_pattern(p2, l2, sat2, base) : ~0ull;
+                    top = top < whi ? top : whi;
                 } else {
                     // The largest element may encode to zero within tau (or
                     // tau is infinite).  From the first code at which every
                     // element encodes to zero (S >= 4 a_b is enough) all
                     // larger codes tie with it, so the candidates are the
-                    // codes from 1 up to a bound on that code.
-                    int up = TOP;
+                    // codes of the window up to a bound on that code.
+                    int up = whi;
                     if (tau < __builtin_inff()) {
-                        up = e4m3_code_ceil_sub(a_b * inv_four_g * 16.0f * (1.0f + 0x1p-18f));
-                        up = up < TOP ? up : TOP;
+                        const int z = e4m3_code_ceil_sub(a_b * inv_four_g * 16.0f * (1.0f + 0x1p-18f));
+                        up = z < up ? z : up;
                     }
-                    base = 1;
-                    mask = frame_bits(1, up, 1);
-                    const int d1 = (int)c1 - 1, d2 = (int)c2 - 1;
-                    if (d1 <= 63) mask &= ~(1ull << d1);
-                    if (d2 <= 63) mask &= ~(1ull << d2);
-                    ovf = up - 64 > 0 ? up - 64 : 0;
+                    base = wlo;
+                    mask = ~0ull;
+                    top = up;
                 }
+                // codes wlo .. min(top, whi) only, and not the two starts
+                if (base < wlo) mask &= wlo - base < 64 ? ~0ull << (wlo - base) : 0ull;
+                top = top < whi ? top : whi;
+                mask = top < base ? 0ull : mask & low_bits(top - base);
+                if (base == 0) mask &= ~1ull;
+                const int d1 = (int)c1 - base, d2 = (int)c2 - base;
+                if (d1 >= 0 && d1 <= 63) mask &= ~(1ull << d1);
+                if (d2 >= 0 && d2 <= 63) mask &= ~(1ull << d2);
+                ovf = top - (base + 63) > 0 ? top - (base + 63) : 0;
                 n[b] = (uint32_t)__popcll(mask) + (uint32_t)ovf;
             }
         }
@@ -1276,8 +1310,12 @@ __device__ __forceinline__ void bf_search_tile_mask(const float (&y)[U], bool ac
         unsigned long long m;
         int base, ovf_pos;
         auto load_block = [&](uint32_t kk) {
-            const float4 v = *reinterpret_cast<const float4*>(W.tile + (kk / NB) * SLOT + (kk % NB) * B * 4);
-            yk[0] = v.x; yk[1] = v.y; yk[2] = v.z; yk[3] = v.w;
+            const float4* src = reinterpret_cast<const float4*>(W.tile + (kk / NB) * SLOT + (kk % NB) * B * 4);
+#pragma unroll
+            for (int i = 0; i < B / 4; ++i) {
+                const float4 v = src[i];
+                yk[4 * i] = v.x; yk[4 * i + 1] = v.y; yk[4 * i + 2] = v.z; yk[4 * i + 3] = v.w;
+            }
             m = W.mask[kk];
             base = W.mbase[kk];
             ovf_pos = 0;
@@ -1445,8 +1483,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_bf(QuantArgs p) {
             bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
         }
         bool nan_blk[NB];
-        if constexpr (B == 4 && SF == SF_E4M3) {
-            if (fast) bf_search_tile_mask<U>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+        if constexpr ((B == 4 || B == 8) && SF == SF_E4M3) {
+            if (fast) bf_search_tile_mask<U, B>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
             else bf_search_tile<SF, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
         } else {
             if (fast) bf_search_tile<SF, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
@@ -1531,8 +1569,8 @@ __global__ __launch_bounds__(kThreads) void k_gsearch_bf(GSearchArgs p) {
             float y[U];
             bf_load_tile<InT, U, H>(p, u0, nvalid, lane, W.tile, y);
             bool nan_blk[NB];
-            if constexpr (B == 4) {
-                if (fast) bf_search_tile_mask<U>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
+            if constexpr (B == 4 || B == 8) {
+                if (fast) bf_search_tile_mask<U, B>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
                 else bf_search_tile<SF_E4M3, B, U, false>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
             } else {
                 if (fast) bf_search_tile<SF_E4M3, B, U, true>(y, active, g, inv_six_g, inv_four_g, s_bf, W, lane, nan_blk);
