@@ -983,10 +983,16 @@ def main():
         sel = [c for _, calls in configs.values() for c in calls if any(pt in c.name for pt in pats)]
         print(f"[bench] profiling {len(sel)} calls x {args.steps}: {[c.name for c in sel][:6]}", file=sys.stderr,
               flush=True)
+        if args.copy_mb:
+            src = torch.empty(args.copy_mb << 18, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            src.fill_(1.0)
         torch.cuda.synchronize()
         for _ in range(args.steps):
             for c in sel:
                 c()
+            if args.copy_mb:
+                dst.copy_(src)
         torch.cuda.synchronize()
         print("[bench] profiling run done", file=sys.stderr, flush=True)
         return
