@@ -66,9 +66,15 @@ __device__ __forceinline__ float group_tree_sum(float v) {
 // stride h < E run inside the lane, the stages with h >= E pair lane l with
 // lane l ^ (h / E).  The lower element of a pair becomes fl(a + b), the
 // upper fl(a - b), a the lower and b the upper value, as in the in-lane
-// stages; then every value is multiplied once by fl(1 / sqrt(H)) (a NaN
-// leaves as the positive quiet NaN, as in fwht_segments).
-template <int H, int E>
+// stages.  Across lanes both are one addition: the lower lane adds its
+// partner's b to its a, the upper lane adds its partner's a to -b (IEEE
+// defines a - b as a + (-b), signed zeros included).  With SCALE every value
+// is then multiplied once by fl(1 / sqrt(H)); without it the caller applies
+// that factor (the abs-max pre-pass scales only its maximum, which gives
+// the same bits because rounding is monotone).  NaN signs are left as the
+// arithmetic makes them: the quantizer canonicalises the elements of a NaN
+// block, the only place where the sign of a NaN reaches an output.
+template <int H, int E, bool SCALE = true>
 __device__ __forceinline__ void fwht_chunk(float (&y)[E], int lane) {
     static_assert(H % E == 0 && H / E <= 8, "segments of 1 to 8 chunks");
 #pragma unroll
@@ -85,19 +91,16 @@ __device__ __forceinline__ void fwht_chunk(float (&y)[E], int lane) {
     static_for<3>([&](auto si) {
         constexpr int m = 1 << decltype(si)::value;     // lane distance of this stage
         if constexpr (m < H / E) {
-            const bool upper = (lane & m) != 0;
+            const uint32_t flip = (lane & m) ? 0x80000000u : 0u;
 #pragma unroll
-            for (int i = 0; i < E; ++i) {
-                const float other = lane_xor_f32<m>(y[i]);
-                const float lo = y[i] + other;            // this lane holds a, the partner b
-                const float hi = other - y[i];            // the partner holds a, this lane b
-                y[i] = upper ? hi : lo;
-            }
+            for (int i = 0; i < E; ++i) y[i] = lane_xor_f32<m>(y[i]) + as_f(as_u(y[i]) ^ flip);
         }
     });
-    constexpr float c = hadamard_coef<H>();
+    if constexpr (SCALE) {
+        constexpr float c = hadamard_coef<H>();
 #pragma unroll
-    for (int i = 0; i < E; ++i) y[i] = rotated_nan_canonical(y[i] * c);
+        for (int i = 0; i < E; ++i) y[i] *= c;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -225,12 +228,16 @@ __device__ __forceinline__ float encode_hw_tab(const float (&y)[E], float S, flo
 }
 
 // The nibbles (sign only) and values (NaN with the sign) of a NaN block part.
-template <int BL, int OFF, int E>
+// ROT: the values come from the rotation, whose NaNs count as the positive
+// quiet NaN (IEEE 754 leaves the sign of an arithmetic NaN open, gfx950's
+// subtraction flips it where x86's keeps it, and here it reaches the code).
+template <int BL, int OFF, bool ROT, int E>
 __device__ __forceinline__ void nan_block_hw(const float (&y)[E], uint32_t& cw, float (&p)[E]) {
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-        cw |= (as_u(y[OFF + i]) >> 31) << (4 * (OFF + i) + 3);
-        p[OFF + i] = canonical_nan_like(y[OFF + i]);
+        const float v = ROT ? rotated_nan_canonical(y[OFF + i]) : y[OFF + i];
+        cw |= (as_u(v) >> 31) << (4 * (OFF + i) + 3);
+        p[OFF + i] = canonical_nan_like(v);
     }
 }
 
@@ -239,9 +246,10 @@ __device__ __forceinline__ void nan_block_hw(const float (&y)[E], uint32_t& cw, 
 // a block inside this lane (min(B, E)), LB = lanes a block spans; the chunk
 // holds E / BL (partial) blocks.  Outputs: the chunk's code word (E
 // nibbles), the dequantized values p, each block's scale code and SSE
-// (whole block, every lane of it).
+// (whole block, every lane of it).  ROT: y comes from the rotation, whose
+// NaNs count as the positive quiet NaN.
 // ---------------------------------------------------------------------------
-template <int SF, int ST, int B, int E>
+template <int SF, int ST, int B, int E, bool ROT>
 __device__ __forceinline__ void quant_chunk(const float (&y)[E], const ScaleCtx& cx, int prevent_zero,
                                             const uint32_t (&given)[(E + B - 1) / B], uint32_t& cw, float (&p)[E],
                                             uint32_t (&sc)[(E + B - 1) / B], float (&sse)[(E + B - 1) / B]) {
@@ -256,15 +264,20 @@ __device__ __forceinline__ void quant_chunk(const float (&y)[E], const ScaleCtx&
         uint32_t code = 0;
         bool nanb;
         if constexpr (ST == ST_GIVEN) {
+            // a NaN element encodes as a zero of its sign here, so a rotated
+            // NaN takes its canonical (positive) sign first
+            float yc[E];
+#pragma unroll
+            for (int i = 0; i < E; ++i) yc[i] = ROT ? rotated_nan_canonical(y[i]) : y[i];
             if constexpr (SF == SF_E8M0) {
                 code = given[b] & 0xFFu;
                 nanb = code == kE8M0NaN;
-                if (!nanb) e = encode_hw<QM_E8M0, BL, OFF, true>(y, e8m0_value(code), e8m0_inverse(code), cw, p);
+                if (!nanb) e = encode_hw<QM_E8M0, BL, OFF, true>(yc, e8m0_value(code), e8m0_inverse(code), cw, p);
             } else {
                 code = given[b] & scale_code_mask<SF>();
                 const float2 sr = cx.tab->sr[code];
                 nanb = code == scale_nan<SF>() || !scale_usable(sr.x);
-                if (!nanb) e = encode_hw_tab<BL, OFF, true>(y, sr.x, sr.y, cw, p);
+                if (!nanb) e = encode_hw_tab<BL, OFF, true>(yc, sr.x, sr.y, cw, p);
             }
             // a caller-given scale needs no cross-lane choice; the SSE still
             // sums over the whole block
@@ -308,7 +321,7 @@ __device__ __forceinline__ void quant_chunk(const float (&y)[E], const ScaleCtx&
             }
         }
         if (nanb) {
-            nan_block_hw<BL, OFF>(y, cw, p);
+            nan_block_hw<BL, OFF, ROT>(y, cw, p);
             e = as_f(kQNaN);
         }
         sc[b] = code;
@@ -480,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void k_qstream(QuantArgs p) {
 
             uint32_t cw, sc[NB];
             float dq[E], sse[NB];
-            quant_chunk<SF, ST, B, E>(y, cx, p.prevent_zero, given, cw, dq, sc, sse);
+            quant_chunk<SF, ST, B, E, (H > 0)>(y, cx, p.prevent_zero, given, cw, dq, sc, sse);
             if (!FULL && j >= nchunks) continue;
             const int64_t e0 = j * E;                 // dense element index of the chunk
             if (p.codes) store_code_word<E>(p.codes, e0, cw);
@@ -556,12 +569,18 @@ __global__ __launch_bounds__(kThreads) void k_amax_stream(AmaxArgs p) {
         for (int k = 0; k < R; ++k) {
             float y[E];
             widen_chunk<InT, E>(raw[k], y);
-            if constexpr (H > 0) fwht_chunk<H, E>(y, lane);
+            if constexpr (H > 0) fwht_chunk<H, E, false>(y, lane);
 #pragma unroll
             for (int i = 0; i < E; ++i) m = max(m, as_u(y[i]) & 0x7FFFFFFFu);
         }
 #pragma unroll
         for (int k = 0; k < R; ++k) raw[k] = nxt[k];
+    }
+    // the rotation's factor fl(1 / sqrt(H)), applied to the maximum only:
+    // rounding is monotone, so fl(c max |v|) = max fl(c |v|); an infinite
+    // or NaN maximum stays one, which is all the per-tensor scale reads
+    if constexpr (H > 0) {
+        if (m < 0x7F800000u) m = as_u(as_f(m) * hadamard_coef<H>());
     }
     m = workgroup_max_u32(m);
     if (threadIdx.x == 0) p.partials[blockIdx.x] = m;
