@@ -691,6 +691,34 @@ int oracle_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uin
     return 0;
 }
 
+/* FP4 GEMM on NVFP4 operands ([MR-GPTQ] section 2.3: QuTLASS multiplies
+ * both MXFP4 and NVFP4 operands): C[m][n] = sum over k of dq(A)[m][k] *
+ * dq(B)[n][k], with dq the NVFP4 decode that oracle_dequantize applies: the
+ * E2M1 grid value times S = fl(dec(scale) * g) of its 16-element block
+ * (E4M3 scale, per-tensor g of that operand), rounded to fp32 (NaN for
+ * scale 0x7F).  A codes [M, K/2] + scales [M, K/16], B likewise [N, ...];
+ * products and sum in fp64 (the decoded values are fp32, so every product
+ * is exact in fp64 and C is the exact dot product rounded once per
+ * addition). */
+int oracle_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float g_a, const uint8_t* b_codes,
+                      const uint8_t* b_scales, float g_b, int64_t M, int64_t N, int64_t K, double* c)
+{
+    if (K % 16) return -1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                uint8_t ab = a_codes[m * (K / 2) + k / 2], bb = b_codes[n * (K / 2) + k / 2];
+                int qa = (k & 1) ? (ab >> 4) : (ab & 15), qb = (k & 1) ? (bb >> 4) : (bb & 15);
+                float sa = stored_scale(SF_E4M3, a_scales[m * (K / 16) + k / 16], g_a);
+                float sb = stored_scale(SF_E4M3, b_scales[n * (K / 16) + k / 16], g_b);
+                acc += (double)decode_elem(qa, sa) * (double)decode_elem(qb, sb);
+            }
+            c[m * N + n] = acc;
+        }
+    return 0;
+}
+
 /* FOCUS relaxed fake-quant forward ([FOCUS] methods 2-3): per sub-block k of
  * K values, S_q = fl(S_dq * c_k) with c_k an FP16 coefficient; the element
  * is encoded with u = fl(W / S_q) (0 when S_q is 0) and dequantized with the

@@ -74,6 +74,8 @@ def lib():
         L.oracle_global_scale_search.restype = f
         L.oracle_code_histogram.argtypes, L.oracle_code_histogram.restype = [p, i64, i64, p], i
         L.oracle_mxfp4_gemm.argtypes, L.oracle_mxfp4_gemm.restype = [p, p, p, p, i64, i64, i64, p], i
+        L.oracle_nvfp4_gemm.argtypes = [p, p, f, p, p, f, i64, i64, i64, p]
+        L.oracle_nvfp4_gemm.restype = i
         L.oracle_quantize.argtypes = [i, i, i, i, f, i, p, i, i64, i64, i64,
                                       p, p, p, p, i, i64, p, p]
         L.oracle_quantize.restype = i
@@ -253,6 +255,19 @@ def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales) -> np.ndarray:
     c = np.zeros((M, N), np.float64)
     if lib().oracle_mxfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K, _ptr(c)) != 0:
         raise ValueError("oracle_mxfp4_gemm rejected its arguments")
+    return c
+
+
+def nvfp4_gemm(a_codes, a_scales, g_a, b_codes, b_scales, g_b) -> np.ndarray:
+    """C = dq(A) dq(B)^T in fp64 for NVFP4 operands (codes [rows, K/2], E4M3
+    scales [rows, K/16], per-tensor scales g_a, g_b)."""
+    a_codes, b_codes = (np.ascontiguousarray(t, dtype=np.uint8) for t in (a_codes, b_codes))
+    a_scales, b_scales = (np.ascontiguousarray(t, dtype=np.uint8) for t in (a_scales, b_scales))
+    M, N, K = a_codes.shape[0], b_codes.shape[0], 2 * a_codes.shape[1]
+    c = np.zeros((M, N), np.float64)
+    if lib().oracle_nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), float(g_a), _ptr(b_codes), _ptr(b_scales),
+                               float(g_b), M, N, K, _ptr(c)) != 0:
+        raise ValueError("oracle_nvfp4_gemm rejected its arguments")
     return c
 
 
