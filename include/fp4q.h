@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 7
+#define FP4Q_ABI_VERSION 8
 
 typedef enum {
     FP4Q_OK = 0,
@@ -297,6 +297,34 @@ size_t fp4q_mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 fp4q_status fp4q_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                             const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c, int c_dt,
                             int64_t ldc, void* workspace, void* stream);
+
+/* FP4 GEMM on NVFP4 operands (the MR-GPTQ page, section 2.3: QuTLASS runs
+ * the FP4 matrix products on MXFP4 and on NVFP4 operands):
+ *   C[m][n] = sum_k dq(A)[m][k] * dq(B)[n][k]
+ * with dq the NVFP4 decode that fp4q_dequantize applies for {E4M3, 16}: the
+ * E2M1 value times fl(dec(scale) * g) of its 16-element block (NaN for
+ * scale 0x7F).  A codes [M, K/2] + E4M3 scales [M, K/16] with per-tensor
+ * scale *a_g, B likewise with *b_g (device fp32 scalars as fp4q_quantize
+ * writes them; NULL means 1): the layouts fp4q_quantize writes for
+ * {E4M3, 16}.  C [M, ldc] of type c_dt (FP4Q_F32 or FP4Q_BF16, rounded
+ * half-to-even), ldc >= N.  gfx950's block-scaled matrix cores take only
+ * power-of-two scales per 32 values, so the operands are decoded to fp16
+ * (grid value times dec(scale), exact) and multiplied on the fp16 matrix
+ * cores with fp32 accumulation in an order of their own; the result is then
+ * multiplied by fl(g_a g_b), so it differs from the definition by the
+ * accumulation order and a few roundings of g (relative 2^-22 of the sum
+ * of |products|).  workspace: fp4q_nvfp4_gemm_workspace_bytes(M, N, K)
+ * bytes, 256-byte aligned, owned by the caller (rearranged scales, and
+ * padded operand copies when K is not a multiple of 256; no initialisation
+ * needed, dead after the call).  K must be a positive multiple of 16 and
+ * M * Kp / 2, N * Kp / 2 below 2^32, Kp = K rounded up to a multiple of 256
+ * (FP4Q_ERR_SHAPE); codes and C 16-byte aligned, ldc * element size a
+ * multiple of 16, scales 4-byte aligned, workspace 256-byte aligned
+ * (FP4Q_ERR_ALIGNMENT). */
+size_t fp4q_nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+fp4q_status fp4q_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g,
+                            const uint8_t* b_codes, const uint8_t* b_scales, const float* b_g, int64_t M, int64_t N,
+                            int64_t K, void* c, int c_dt, int64_t ldc, void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

@@ -502,4 +502,28 @@ fp4q_status fp4q_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, con
                                            (hipStream_t)stream));
 }
 
+size_t fp4q_nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return 0;
+    return nvfp4_gemm_workspace(M, N, K);
+}
+
+fp4q_status fp4q_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g,
+                            const uint8_t* b_codes, const uint8_t* b_scales, const float* b_g, int64_t M, int64_t N,
+                            int64_t K, void* c, int c_dt, int64_t ldc, void* workspace, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return FP4Q_ERR_INVALID_ARG;
+    if (c_dt != FP4Q_F32 && c_dt != FP4Q_BF16) return FP4Q_ERR_INVALID_ARG;
+    if (K % 16 != 0) return FP4Q_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP4Q_OK;
+    if (K == 0 || ldc < N) return FP4Q_ERR_SHAPE;
+    const uint64_t kp = (uint64_t)(K + 255) / 256 * 256;      // K as the matrix cores run it
+    if ((uint64_t)M * (kp / 2) >= (1ull << 32) || (uint64_t)N * (kp / 2) >= (1ull << 32)) return FP4Q_ERR_SHAPE;
+    if (!c || !a_codes || !a_scales || !b_codes || !b_scales || !workspace) return FP4Q_ERR_INVALID_ARG;
+    if (!aligned16(c) || (ldc * elem_size(c_dt)) % 16 != 0) return FP4Q_ERR_ALIGNMENT;
+    if (!aligned16(a_codes) || !aligned16(b_codes) || ((uintptr_t)a_scales & 3u) || ((uintptr_t)b_scales & 3u) ||
+        ((uintptr_t)workspace & 255u) || ((uintptr_t)a_g & 3u) || ((uintptr_t)b_g & 3u))
+        return FP4Q_ERR_ALIGNMENT;
+    return device_status(launch_nvfp4_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, M, N, K, c, c_dt, ldc,
+                                           workspace, (hipStream_t)stream));
+}
+
 }  // extern "C"

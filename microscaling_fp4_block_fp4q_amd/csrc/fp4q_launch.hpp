@@ -27,6 +27,10 @@ hipError_t launch_gsearch_pick(const double* totals, int64_t stride, const uint3
 size_t mxfp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mxfp4_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t M,
                              int64_t N, int64_t K, void* c, int c_dt, int64_t ldc, void* workspace, hipStream_t s);
+size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
+hipError_t launch_nvfp4_gemm(const uint8_t* a, const uint8_t* as, const float* ga, const uint8_t* b,
+                             const uint8_t* bs, const float* gb, int64_t M, int64_t N, int64_t K, void* c, int c_dt,
+                             int64_t ldc, void* workspace, hipStream_t s);
 hipError_t launch_code_hist(const uint8_t* codes, int64_t nbytes, unsigned long long* counts, int grid,
                             hipStream_t s);
 hipError_t launch_amax(const AmaxArgs& a, int x_dt, int H, int grid, hipStream_t s);

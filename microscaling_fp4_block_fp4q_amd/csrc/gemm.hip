@@ -424,6 +424,240 @@ __global__ __launch_bounds__(256, 1) void k_mxfp4_gemm(GemmArgs p) {
     else gemm_store<uint16_t>(p, acc, buf, r0, c0, lane, full);
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 operands: E4M3 block scales per 16 values and a per-tensor scale g
+// per operand (the NVFP4 matrix products QuTLASS runs, MR-GPTQ page,
+// section 2.3).  gfx950's block-scaled matrix cores take only power-of-two
+// scales per 32 values, so this kernel decodes each operand to fp16 and
+// runs the fp16 matrix cores (v_mfma_f32_32x32x16_f16): a value is
+// grid * dec(s), E2M1 value times E4M3 scale, which has at most six
+// significant bits and lies in [2^-10, 2688], so fp16 holds it exactly and
+// every product is exact in the fp32 accumulation; g_a g_b multiplies the
+// result once.  The decode: the scaled FP4 -> fp16 convert with the
+// power-of-two part P = 2^(max(e, 1) - 7) of the scale (the convert applies
+// only a scale's exponent), then one packed fp16 multiply by the mantissa
+// part mu = dec(s) / P (1 + m / 8, or m / 8 for the subnormal codes; NaN
+// for code 0x7F).  P and mu of all 128 codes sit in an LDS table.
+//
+// Codes are staged exactly as in the MXFP4 kernel (same tiles, stages,
+// direct loads, XOR swizzle and fragment reads).  A lane's 16-byte
+// fragment chunk holds 32 K values (two 16-value scale blocks); each of its
+// four dwords (8 values) is the lane's part of one 32 x 32 x 16 product,
+// the same dword of A and of B in the same product, so the products sum
+// matching K indices (the K order inside a step is permuted alike for both
+// operands, which leaves the dot product's terms unchanged).
+//
+// Scales: a pass rewrites each operand's [rows, K/16] scale bytes so that a
+// lane loads, per fragment and step, the 8 scale bytes of its chunks' blocks
+// (byte 2 h + j: block 4 h + 2 (l / 32) + j of the step) in one 8-byte load.
+// ---------------------------------------------------------------------------
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+struct NvGemmArgs {
+    GemmArgs g;                                  // sa / sb: the rearranged scale bytes (as uint2)
+    const float* ga;                             // per-tensor scales (device scalars; null: 1)
+    const float* gb;
+};
+
+// out[(f * T + t) * 64 + l] = the 8 scale bytes of lane l of fragment f at
+// step t: byte 2 h + j = block 16 t + 4 h + 2 (l / 32) + j of row
+// 32 f + l % 32; rows past the matrix get code 0x38 (1.0).
+__global__ void k_gemm_shuffle_scales_nv(const uint8_t* __restrict__ s, int64_t rows, int64_t kblocks, int steps,
+                                         int64_t total, uint2* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int l = (int)(i & 63);
+    const int64_t ft = i >> 6;
+    const int t = (int)(ft % steps);
+    const int64_t row = (ft / steps) * 32 + (l & 31);
+    uint2 w = make_uint2(0x38383838u, 0x38383838u);
+    if (row < rows) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(s + row * kblocks + 16 * t);
+        const uint32_t q0 = p[0], q1 = p[1], q2 = p[2], q3 = p[3];   // blocks 4 h .. 4 h + 3 in q_h
+        const uint32_t sel = (l >> 5) ? 0x07060302u : 0x05040100u;  // bytes 2 (l / 32) + {0, 1} of each
+        w = make_uint2(__builtin_amdgcn_perm(q1, q0, sel), __builtin_amdgcn_perm(q3, q2, sel));
+    }
+    out[i] = w;
+}
+
+// Decode table entry of E4M3 code c = (e, m): P's fp32 bits (low 16 bits
+// zero) with mu's fp16 bits in the low half.
+__device__ __forceinline__ uint32_t nv_table_entry(uint32_t c) {
+    const uint32_t e = c >> 3, m = c & 7u;
+    const uint32_t p_bits = ((e > 0u ? e : 1u) + 120u) << 23;
+    const float mu = (float)(e > 0u ? 8u + m : m) * 0.125f;
+    uint32_t mu_bits = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)mu);
+    if (c == 0x7Fu) mu_bits = 0x7E00u;           // NaN scale: every value NaN
+    return p_bits | mu_bits;
+}
+
+__shared__ uint32_t g_nv_table[128];
+
+// The fp16 operand of one 32 x 32 x 16 product: dword d of a fragment chunk
+// (8 codes, byte k = values 2 k and 2 k + 1) decoded with table entry w.
+__device__ __forceinline__ v8h nv_operand(uint32_t d, uint32_t w) {
+    const float P = __builtin_bit_cast(float, w & 0xFFFF0000u);
+    const v2h mu = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(w, w, 0x01000100u));
+    const v2h x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, P, 0) * mu;
+    const v2h x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, P, 1) * mu;
+    const v2h x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, P, 2) * mu;
+    const v2h x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, P, 3) * mu;
+    return v8h{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+}
+
+struct NvScales {
+    uint2 a[4], b[4];
+};
+
+__device__ __forceinline__ void nv_issue_scales(const GemmArgs& p, const uint2* sa, const uint2* sb, int t,
+                                                int64_t fa0, int64_t fb0, NvScales& sc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t fa = min<int64_t>(fa0 + i, p.frags_a - 1) - fa0;
+        const int64_t fb = min<int64_t>(fb0 + i, p.frags_b - 1) - fb0;
+        sc.a[i] = sa[(fa * p.steps + t) * 64];
+        sc.b[i] = sb[(fb * p.steps + t) * 64];
+    }
+}
+
+// Table entry of scale byte 2 h + j of a lane's 8 bytes.
+template <int H, int J>
+__device__ __forceinline__ uint32_t nv_entry(const uint2& b) {
+    constexpr int k = 2 * H + J;
+    const uint32_t w = k < 4 ? b.x : b.y;
+    return g_nv_table[(w >> (8 * (k & 3))) & 0x7Fu];
+}
+
+// Substep H of a step: the four 32 x 32 x 16 products of each fragment pair.
+template <int H>
+__device__ __forceinline__ void nv_mfma(const GemmFrags& fr, const NvScales& sc, v16f (&acc)[4][4]) {
+    uint32_t ea[4][2], eb[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ea[i][0] = nv_entry<H, 0>(sc.a[i]);
+        ea[i][1] = nv_entry<H, 1>(sc.a[i]);
+        eb[i][0] = nv_entry<H, 0>(sc.b[i]);
+        eb[i][1] = nv_entry<H, 1>(sc.b[i]);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        v8h oa[4], ob[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            oa[i] = nv_operand((uint32_t)fr.a[i][d], ea[i][d >> 1]);
+            ob[i] = nv_operand((uint32_t)fr.b[i][d], eb[i][d >> 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ob[j], oa[i], acc[i][j], 0, 0, 0);
+    }
+}
+
+// One step, staged as gemm_step (the same loads, reads and barrier), with
+// the fp16 products of each substep.
+template <int S>
+__device__ __forceinline__ void nv_step(const GemmArgs& p, const GemmLane& L, const uint2* sa, const uint2* sb,
+                                        int t, int wave, int lane, int wm, int wn, int64_t fa0, int64_t fb0,
+                                        NvScales& sc, GemmFrags& f0, v16f (&acc)[4][4]) {
+    GemmFrags f1;
+    gemm_issue_codes<S ^ 1, kHalfDma, kGemmDmaPerOperand>(L, min(t + 1, p.steps - 1), wave);
+    gemm_read<S>(f1, 1, lane, wm, wn);
+    nv_mfma<0>(f0, sc, acc);
+    gemm_read<S>(f0, 2, lane, wm, wn);
+    nv_mfma<1>(f1, sc, acc);
+    gemm_read<S>(f1, 3, lane, wm, wn);
+    nv_mfma<2>(f0, sc, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_wait_barrier<0>();
+    gemm_issue_codes<S, 0, kHalfDma>(L, min(t + 2, p.steps - 1), wave);
+    gemm_read<S ^ 1>(f0, 0, lane, wm, wn);
+    nv_mfma<3>(f1, sc, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    nv_issue_scales(p, sa, sb, min(t + 2, p.steps - 1), fa0, fb0, sc);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int PARITY>
+__global__ __launch_bounds__(256, 1) void k_nvfp4_gemm(NvGemmArgs q) {
+    const GemmArgs& p = q.g;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    if (tid < 128) g_nv_table[tid] = nv_table_entry((uint32_t)tid);
+    int tm, tn;
+    gemm_tile(p, tm, tn);
+    const int64_t m0 = (int64_t)tm * kGemmTile, n0 = (int64_t)tn * kGemmTile;
+    const int64_t fa0 = (m0 + 128 * wm) / 32, fb0 = (n0 + 128 * wn) / 32;
+    const int nt = p.steps;
+    const uint2* sa = reinterpret_cast<const uint2*>(p.sa) + fa0 * nt * 64 + lane;
+    const uint2* sb = reinterpret_cast<const uint2*>(p.sb) + fb0 * nt * 64 + lane;
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+    const GemmLane L = gemm_lane(p, m0, n0, wave, lane, wm, wn);
+    NvScales s0, s1;
+    gemm_issue_codes<0>(L, 0, wave);
+    nv_issue_scales(p, sa, sb, 0, fa0, fb0, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_issue_codes<1, 0, kHalfDma>(L, min(1, nt - 1), wave);
+    nv_issue_scales(p, sa, sb, min(1, nt - 1), fa0, fb0, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_wait_barrier<kGemmDmaPerOperand + 8>();    // all but step 1's half and its 8 scale loads (also the table)
+    GemmFrags f0;
+    gemm_read<0>(f0, 0, lane, wm, wn);
+    if constexpr (PARITY == 1) {
+        nv_step<0>(p, L, sa, sb, 0, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
+#pragma unroll 1
+        for (int t = 1; t < nt; t += 2) {
+            nv_step<1>(p, L, sa, sb, t, wave, lane, wm, wn, fa0, fb0, s1, f0, acc);
+            nv_step<0>(p, L, sa, sb, t + 1, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
+        }
+    } else {
+#pragma unroll 1
+        for (int t = 0; t < nt; t += 2) {
+            nv_step<0>(p, L, sa, sb, t, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
+            nv_step<1>(p, L, sa, sb, t + 1, wave, lane, wm, wn, fa0, fb0, s1, f0, acc);
+        }
+    }
+    gemm_wait_barrier<0>();
+    const float gg = (q.ga ? *q.ga : 1.0f) * (q.gb ? *q.gb : 1.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] *= gg;
+    uint8_t* buf = reinterpret_cast<uint8_t*>(&g_stage0) + wave * (32 * 128 * 4);
+    const int64_t r0 = m0 + 128 * wm, c0 = n0 + 128 * wn;
+    const bool full = m0 + kGemmTile <= p.M && n0 + kGemmTile <= p.N;
+    if (p.c_dt == DT_F32) gemm_store<float>(p, acc, buf, r0, c0, lane, full);
+    else gemm_store<uint16_t>(p, acc, buf, r0, c0, lane, full);
+}
+
+// Copy of an NVFP4 operand with K padded to Kp: block j of a row (16
+// values: 8 code bytes and one scale byte) copied for j < K / 16, code 0
+// (+0) with scale 0x38 (1.0) past it.  One lane per block.
+__global__ void k_gemm_pad_nv(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t rows,
+                              int64_t kb, int64_t kbp, uint8_t* __restrict__ pcodes, uint8_t* __restrict__ pscales) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= rows * kbp) return;
+    const int64_t r = i / kbp, j = i - r * kbp;
+    uint2 v = make_uint2(0u, 0u);
+    uint8_t sc = 0x38;
+    if (j < kb) {
+        v = *reinterpret_cast<const uint2*>(codes + (r * kb + j) * 8);
+        sc = scales[r * kb + j];
+    }
+    *reinterpret_cast<uint2*>(pcodes + i * 8) = v;
+    pscales[i] = sc;
+}
+
 // Copy of an operand with K padded to Kp (a multiple of the K-step): block
 // j of a row (32 values: 16 code bytes and one scale byte) is copied for
 // j < K / 32, and the padding holds code 0 (+0, which adds exactly 0 to
@@ -525,6 +759,76 @@ hipError_t launch_mxfp4_gemm_padded_k(const uint8_t* a, const uint8_t* as, const
     return launch_mxfp4_gemm(pa, pas, pb, pbs, M, N, Kp, c, c_dt, ldc, workspace, s);
 }
 
+// Bytes of the rearranged NVFP4 scales of both operands (K a multiple of the K-step).
+size_t shuffled_scales_bytes_nv(int64_t M, int64_t N, int64_t K) {
+    const int64_t steps = K / kGemmStepK;
+    const auto part = [&](int64_t rows) { return (size_t)round256(((rows + 31) / 32) * steps * 512); };
+    return part(M) + part(N);
+}
+
 }  // namespace
+
+size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+    if (K % kGemmStepK == 0) return shuffled_scales_bytes_nv(M, N, K);
+    const int64_t Kp = (K + kGemmStepK - 1) / kGemmStepK * kGemmStepK;
+    return shuffled_scales_bytes_nv(M, N, Kp) + (size_t)(round256(M * Kp / 2) + round256(N * Kp / 2) +
+                                                         round256(M * Kp / 16) + round256(N * Kp / 16));
+}
+
+hipError_t launch_nvfp4_gemm(const uint8_t* a, const uint8_t* as, const float* ga, const uint8_t* b,
+                             const uint8_t* bs, const float* gb, int64_t M, int64_t N, int64_t K, void* c, int c_dt,
+                             int64_t ldc, void* workspace, hipStream_t s) {
+    if (K % kGemmStepK != 0) {
+        // pad K to the K-step: copies of both operands after the rearranged scales
+        const int64_t Kp = (K + kGemmStepK - 1) / kGemmStepK * kGemmStepK;
+        uint8_t* w = reinterpret_cast<uint8_t*>(workspace) + shuffled_scales_bytes_nv(M, N, Kp);
+        uint8_t* pa = w;
+        uint8_t* pb = pa + round256(M * Kp / 2);
+        uint8_t* pas = pb + round256(N * Kp / 2);
+        uint8_t* pbs = pas + round256(M * Kp / 16);
+        const int64_t kb = K / 16, kbp = Kp / 16;
+        const auto pad = [&](const uint8_t* codes, const uint8_t* scales, int64_t rows, uint8_t* pc, uint8_t* ps) {
+            const int64_t n = rows * kbp;
+            hipLaunchKernelGGL(k_gemm_pad_nv, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, scales, rows,
+                               kb, kbp, pc, ps);
+        };
+        pad(a, as, M, pa, pas);
+        pad(b, bs, N, pb, pbs);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_nvfp4_gemm(pa, pas, ga, pb, pbs, gb, M, N, Kp, c, c_dt, ldc, workspace, s);
+    }
+    NvGemmArgs q{};
+    GemmArgs& p = q.g;
+    p.a = a;
+    p.b = b;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.c = c;
+    p.c_dt = c_dt;
+    p.ldc = ldc;
+    p.tiles_m = (int)((M + kGemmTile - 1) / kGemmTile);
+    p.tiles_n = (int)((N + kGemmTile - 1) / kGemmTile);
+    p.steps = (int)(K / kGemmStepK);
+    p.frags_a = (int)((M + 31) / 32);
+    p.frags_b = (int)((N + 31) / 32);
+    const size_t wa = ((size_t)p.frags_a * p.steps * 512 + 255) / 256 * 256;
+    uint2* sa = reinterpret_cast<uint2*>(workspace);
+    uint2* sb = reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(workspace) + wa);
+    const int64_t ta = (int64_t)p.frags_a * p.steps * 64, tb = (int64_t)p.frags_b * p.steps * 64;
+    hipLaunchKernelGGL(k_gemm_shuffle_scales_nv, dim3((unsigned)((ta + 255) / 256)), dim3(256), 0, s, as, M, K / 16,
+                       p.steps, ta, sa);
+    hipLaunchKernelGGL(k_gemm_shuffle_scales_nv, dim3((unsigned)((tb + 255) / 256)), dim3(256), 0, s, bs, N, K / 16,
+                       p.steps, tb, sb);
+    p.sa = reinterpret_cast<const uint32_t*>(sa);
+    p.sb = reinterpret_cast<const uint32_t*>(sb);
+    q.ga = ga;
+    q.gb = gb;
+    const dim3 grid((unsigned)p.tiles_m * p.tiles_n), block(256);
+    if (p.steps % 2) hipLaunchKernelGGL(k_nvfp4_gemm<1>, grid, block, 0, s, q);
+    else hipLaunchKernelGGL(k_nvfp4_gemm<0>, grid, block, 0, s, q);
+    return hipGetLastError();
+}
 
 }  // namespace fp4q_dev

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "libfp4q.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "fp4q.h")
 
 # FP4Q_ABI_VERSION and the enums (include/fp4q.h)
-ABI_VERSION = 7
+ABI_VERSION = 8
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_ALIGNMENT, ERR_DEVICE, ERR_TOO_LARGE = range(7)
 F32, BF16, F16 = 0, 1, 2
 E8M0, E4M3, UE5M3 = 0, 1, 2
@@ -107,6 +107,10 @@ def lib() -> ctypes.CDLL:
         L.fp4q_mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, ctypes.c_int, i64, p, p]
         L.fp4q_mxfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.fp4q_mxfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fp4q_nvfp4_gemm.restype = ctypes.c_int
+        L.fp4q_nvfp4_gemm.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, ctypes.c_int, i64, p, p]
+        L.fp4q_nvfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
+        L.fp4q_nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         _lib = L
     return _lib
 
@@ -367,6 +371,38 @@ def fp4q_mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, c, workspace, stream=N
     _check(st, "fp4q_mxfp4_gemm")
 
 
+def nvfp4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().fp4q_nvfp4_gemm_workspace_bytes(M, N, K)
+
+
+def _g_ptr(g, name):
+    if g is None:
+        return None
+    _dense(g, torch.float32, (1,), name)
+    return _ptr(g)
+
+
+def fp4q_nvfp4_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, c, workspace, stream=None):
+    """Raw entry point: a_g / b_g are one-element fp32 device tensors (the g
+    fp4q_quantize writes) or None (1)."""
+    if a_codes.dim() != 2 or b_codes.dim() != 2:
+        raise ValueError("codes: expected 2-D tensors [rows, K/2]")
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    K = 2 * a_codes.shape[1]
+    _dense(a_codes, torch.uint8, (M, K // 2), "a_codes")
+    _dense(b_codes, torch.uint8, (N, K // 2), "b_codes")
+    _dense(a_scales, torch.uint8, (M, K // 16), "a_scales")
+    _dense(b_scales, torch.uint8, (N, K // 16), "b_scales")
+    ldc = _out_2d(c, M, N, "c")
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous() \
+            or workspace.numel() * workspace.element_size() < nvfp4_gemm_workspace_bytes(M, N, K):
+        raise ValueError("workspace: expected a contiguous device tensor of nvfp4_gemm_workspace_bytes(M, N, K)")
+    st = lib().fp4q_nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _g_ptr(a_g, "a_g"), _ptr(b_codes), _ptr(b_scales),
+                               _g_ptr(b_g, "b_g"), M, N, K, _ptr(c), dtype_code(c), ldc, _ptr(workspace),
+                               _stream(stream))
+    _check(st, "fp4q_nvfp4_gemm")
+
+
 # --------------------------------------------------------------------------
 # allocating wrappers
 # --------------------------------------------------------------------------
@@ -464,6 +500,24 @@ def code_histogram(codes, stream=None):
 def gemm_workspace(M, N, K, device):
     """Device workspace for fp4q_mxfp4_gemm (256-byte aligned by torch's allocator)."""
     return torch.empty(max(mxfp4_gemm_workspace_bytes(M, N, K), 256), dtype=torch.uint8, device=device)
+
+
+def nvfp4_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, out_dtype=torch.float32, workspace=None,
+               stream=None):
+    """C [M, N] = dq(A) dq(B)^T for NVFP4 operands (codes [rows, K/2], E4M3
+    scales [rows, K/16], per-tensor scales a_g / b_g: one-element fp32 device
+    tensors as quantize() returns them, or None for 1).  C is a view of N
+    columns of an [M, ldc] buffer with rows padded to 16 bytes."""
+    M, N, K = a_codes.shape[0], b_codes.shape[0], 2 * a_codes.shape[1]
+    per16 = 16 // torch.empty(0, dtype=out_dtype).element_size()
+    ldc = (N + per16 - 1) // per16 * per16
+    with _on(stream):
+        c = torch.empty((M, ldc), dtype=out_dtype, device=a_codes.device)[:, :N]
+        if workspace is None:
+            n = nvfp4_gemm_workspace_bytes(M, N, K)
+            workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=a_codes.device)
+        fp4q_nvfp4_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, c, workspace, stream)
+    return c
 
 
 def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.float32, workspace=None, stream=None):

@@ -235,6 +235,60 @@ __global__ __launch_bounds__(kThreads) void k_fp4_convert(unsigned long long* mi
     atomicAdd(&mismatches[2], checked);
 }
 
+// The gfx950 scaled converts FP4 -> bf16 and FP4 -> fp16 (which the NVFP4
+// GEMM dequantizes its operands with): every byte of two nibbles, at each of
+// the four byte positions of the source dword, for the power-of-two part
+// P_c = 2^(max(e, 1) - 7) of every E4M3 block scale code c = (e, m), c =
+// 0..126, against the exact product of the E2M1 value and P_c.  The same
+// converts given the full scale value dec(c) are counted too: they apply
+// only its exponent (as an E8M0 scale would be), which is why the GEMM
+// multiplies the scale's mantissa in separately.  counts: [0] bf16 values
+// that differ (+0 and -0 equal), [1] bf16 bit patterns that differ, [2], [3]
+// the same for fp16, [4] values checked, [5] fp16 values that differ from
+// the exact product when the full dec(c) is passed.
+typedef __bf16 probe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 probe_f16x2 __attribute__((ext_vector_type(2)));
+
+template <int POS>
+__device__ __forceinline__ void scaled_convert_pos(uint32_t byte, float P, float S, unsigned long long (&bad)[6]) {
+    const float grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    const uint32_t src = (0xA5C3E1F7u & ~(0xFFu << (8 * POS))) | (byte << (8 * POS));
+    const probe_bf16x2 hb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, P, POS);
+    const probe_f16x2 hh = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, P, POS);
+    const probe_f16x2 hs = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, S, POS);
+    const uint32_t gb = __builtin_bit_cast(uint32_t, hb), gh = __builtin_bit_cast(uint32_t, hh);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t nib = (byte >> (4 * h)) & 15u;
+        const float mag = grid[nib & 7u], sgn = nib & 8u ? -1.0f : 1.0f;
+        const float want = sgn * mag * P, want_s = sgn * mag * S;
+        const uint32_t wb = as_u(want) >> 16;
+        const uint32_t wh = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)want);
+        const uint32_t xb = (gb >> (16 * h)) & 0xFFFFu, xh = (gh >> (16 * h)) & 0xFFFFu;
+        bad[0] += as_f(xb << 16) != want;
+        bad[1] += xb != wb;
+        bad[2] += (float)__builtin_bit_cast(_Float16, (uint16_t)xh) != want;
+        bad[3] += xh != wh;
+        bad[4] += 1;
+        bad[5] += (float)hs[h] != want_s;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_fp4_scaled_convert(unsigned long long* counts) {
+    const uint32_t code = blockIdx.x, byte = threadIdx.x;
+    const uint32_t e = code >> 3, m = code & 7u;
+    const float S = e == 0u ? (float)m * 0x1p-9f : __builtin_ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+    const float P = __builtin_ldexpf(1.0f, (int)(e > 0u ? e : 1u) - 7);
+    unsigned long long bad[6] = {0, 0, 0, 0, 0, 0};
+    scaled_convert_pos<0>(byte, P, S, bad);
+    scaled_convert_pos<1>(byte, P, S, bad);
+    scaled_convert_pos<2>(byte, P, S, bad);
+    scaled_convert_pos<3>(byte, P, S, bad);
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+        if (bad[i]) atomicAdd(&counts[i], bad[i]);
+}
+
 template <int KIND>
 hipError_t launch_valu(int iters, int grid, float* out, hipStream_t s) {
     hipLaunchKernelGGL(k_valu<KIND>, dim3(grid), dim3(kThreads), 0, s, iters, out);
@@ -271,6 +325,12 @@ int fp4q_probe_fp4_convert(unsigned long long* mismatches, void* stream) {
     const uint64_t threads = (1ull << 32) / 64u;
     hipLaunchKernelGGL(k_fp4_convert, dim3((unsigned)(threads / kThreads)), dim3(kThreads), 0, (hipStream_t)stream,
                        mismatches);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int fp4q_probe_fp4_scaled_convert(unsigned long long* counts, void* stream) {
+    if (!counts) return -1;
+    hipLaunchKernelGGL(k_fp4_scaled_convert, dim3(127), dim3(256), 0, (hipStream_t)stream, counts);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -170,6 +170,35 @@ def test_gemm_validation_and_workspace():
 
 @needs_lib
 @cpu_only
+def test_nvfp4_gemm_validation_and_workspace():
+    L = F.lib()
+    W = F.nvfp4_gemm_workspace_bytes
+    # per operand: ceil(rows / 32) fragments x K / 256 steps x 64 lanes x 8 bytes, each part 256-byte aligned
+    assert W(8192, 8192, 8192) == 2 * (8192 // 32) * 32 * 512
+    assert W(33, 1, 256) == 2 * 512 + 512
+    assert W(4, 4, 40) == 0 and W(0, 4, 256) == 0 and W(4, 4, 0) == 0
+    # K = 272: rearranged scales for K rounded up to 512, then the padded copies of codes (rows x 256
+    # bytes) and scales (rows x 32 bytes), every part 256-byte aligned
+    assert W(33, 1, 272) == (2048 + 1024) + (8448 + 256) + (1280 + 256)
+
+    def g(M=4, N=4, K=256, a=A, sa=A, ga=A, b=A, sb=A, gb=A, c=A, dt=F.F32, ldc=4, ws=A):
+        return L.fp4q_nvfp4_gemm(P(a), P(sa), P(ga), P(b), P(sb), P(gb), M, N, K, P(c), dt, ldc, P(ws), None)
+    assert g(M=0) == F.OK and g(N=0) == F.OK
+    assert g(M=-1) == F.ERR_INVALID_ARG
+    assert g(dt=F.F16) == F.ERR_INVALID_ARG
+    assert g(K=40) == F.ERR_SHAPE and g(K=8) == F.ERR_SHAPE and g(K=0) == F.ERR_SHAPE
+    assert g(ldc=3) == F.ERR_SHAPE
+    assert g(M=1 << 24, K=1 << 9) == F.ERR_SHAPE
+    assert g(M=1 << 24, K=496) == F.ERR_SHAPE                                    # K runs padded to 512
+    assert g(ws=0) == F.ERR_INVALID_ARG and g(a=0) == F.ERR_INVALID_ARG and g(sb=0) == F.ERR_INVALID_ARG
+    assert g(ws=A + 16) == F.ERR_ALIGNMENT
+    assert g(a=A + 8) == F.ERR_ALIGNMENT and g(sa=A + 2) == F.ERR_ALIGNMENT and g(gb=A + 2) == F.ERR_ALIGNMENT
+    assert g(c=A + 4) == F.ERR_ALIGNMENT
+    assert g(ldc=6) == F.ERR_ALIGNMENT
+
+
+@needs_lib
+@cpu_only
 def test_other_entry_points_validation():
     L = F.lib()
     nv, mx = F.nvfp4(), F.mxfp4()
