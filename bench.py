@@ -767,6 +767,41 @@ def time_gemm(F, torch, dev, warm=30, reps=10, rounds=3):
     return out
 
 
+MFMA_FP16_PEAK_TFLOPS = 2500.0              # MI355X dense fp16 matrix peak, published
+
+
+def time_gemm_nvfp4(F, torch, dev, warm=10, reps=10, rounds=2):
+    """NVFP4 GEMM (outside the step): the same shapes with NVFP4 operands
+    (E4M3 scales per 16, tensor-amax g per operand; 4-over-6 for the
+    weights).  The matrix cores take only power-of-two block scales, so the
+    operands are decoded to fp16 and run on the fp16 matrix cores: the peak
+    that bounds it is the dense fp16 one; the FP4 peak is given beside it."""
+    out = {}
+    gen = torch.Generator(device=dev).manual_seed(12)
+    for M, N, K in ((8192, 8192, 8192), (8192, 14336, 4096), (8192, 4096, 14336)):
+        qa = F.quantize(torch.randn((M, K), generator=gen, device=dev), F.nvfp4(), want_mse=False)
+        qb = F.quantize(torch.randn((N, K), generator=gen, device=dev) * 0.02, F.nvfp4(F.FOUR_OVER_SIX),
+                        want_mse=False)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(F.nvfp4_gemm_workspace_bytes(M, N, K), 256), dtype=torch.uint8, device=dev)
+        args = (qa["codes"], qa["scales"], qa["g"], qb["codes"], qb["scales"], qb["g"], c, ws)
+        for _ in range(warm):
+            F.fp4q_nvfp4_gemm(*args)
+        ms = time_fn(torch, lambda: F.fp4q_nvfp4_gemm(*args), rounds * reps)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out[f"{M}x{N}x{K}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                               "mfma_frac": round(tf / MFMA_FP16_PEAK_TFLOPS, 4),
+                               "of_fp4_peak": round(tf / MFMA_FP4_PEAK_TFLOPS, 4)}
+        del qa, qb, c, ws, args
+    out["peak"] = {"TFLOP/s": MFMA_FP16_PEAK_TFLOPS, "what": "MI355X dense fp16 matrix-core peak (the operands "
+                                                              "run decoded to fp16)"}
+    out["what"] = ("not part of the step: NVFP4 GEMM (M x N x K) of NVFP4-quantized N(0,1) activations and "
+                   "N(0,0.02^2) weights (E4M3 scales per 16 values, tensor-amax g), decoded to fp16 on the way "
+                   "to the 32x32x16 fp16 matrix cores, bf16 output, including the per-call scale rearrangement; "
+                   "mean of 20 calls after 10 warm-up calls")
+    return out
+
+
 # --------------------------------------------------------------------------
 # the oracle on the host cores
 # --------------------------------------------------------------------------
@@ -1112,7 +1147,7 @@ def main():
         del cfgs, cbld, flush
         torch.cuda.empty_cache()
     if args.no_extras:
-        search = ue5m3 = hist = gemm = {"what": "not measured (--no-extras)"}
+        search = ue5m3 = hist = gemm = gemm_nv = {"what": "not measured (--no-extras)"}
     else:
         print("[bench] widenings (scale search, UE5M3, histogram, GEMM)", file=sys.stderr, flush=True)
         search = time_quantize_configs(F, torch, X["normal"], [
@@ -1123,6 +1158,7 @@ def main():
             (f"B={B} {STRATS[st]}", F.config(F.UE5M3, B, st)) for B in (16, 4) for st in (0, 2, 3)])
         hist = time_histogram(F, torch, X["normal"])
         gemm = time_gemm(F, torch, dev)
+        gemm_nv = time_gemm_nvfp4(F, torch, dev)
     stream_quant = [(c, ms) for c, ms in per_call if c.meta.get("strategy") in ("absmax", "4-over-6")]
     sb = sum(c.nbytes for c, _ in stream_quant)
     sms = sum(ms for _, ms in stream_quant)
@@ -1170,6 +1206,7 @@ def main():
                                       "UE5M3 block scales (no per-tensor scale), every output"}, **ue5m3),
         "code_histogram": hist,
         "mxfp4_gemm": gemm,
+        "nvfp4_gemm": gemm_nv,
     }
 
     if not args.no_cpu_baseline:

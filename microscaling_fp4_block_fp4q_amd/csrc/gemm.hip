@@ -530,52 +530,98 @@ __device__ __forceinline__ uint32_t nv_entry(const uint2& b) {
     return g_nv_table[(w >> (8 * (k & 3))) & 0x7Fu];
 }
 
-// Substep H of a step: the four 32 x 32 x 16 products of each fragment pair.
-template <int H>
-__device__ __forceinline__ void nv_mfma(const GemmFrags& fr, const NvScales& sc, v16f (&acc)[4][4]) {
-    uint32_t ea[4][2], eb[4][2];
+// A substep's fragment chunks (16 bytes each, no widening).
+struct NvFrags {
+    v4i a[4], b[4];
+};
+
+template <int S>
+__device__ __forceinline__ void nv_read(NvFrags& fr, int h, int lane, int wm, int wn) {
+    const GemmStage& st = gemm_stage<S>();
+    const int r = lane & 31;
+    const int slot = (2 * h + (lane >> 5)) ^ ((r >> 1) & 7);
+    const int off = r * kGemmRowBytes + 16 * slot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        ea[i][0] = nv_entry<H, 0>(sc.a[i]);
-        ea[i][1] = nv_entry<H, 1>(sc.a[i]);
-        eb[i][0] = nv_entry<H, 0>(sc.b[i]);
-        eb[i][1] = nv_entry<H, 1>(sc.b[i]);
+        fr.a[i] = *reinterpret_cast<const v4i*>(st.a + ((128 * wm + 32 * i) * kGemmRowBytes + off));
+        fr.b[i] = *reinterpret_cast<const v4i*>(st.b + ((128 * wn + 32 * i) * kGemmRowBytes + off));
+    }
+}
+
+// The fp16 operands of dword d of every fragment chunk.
+struct NvOps {
+    v8h a[4], b[4];
+};
+
+__device__ __forceinline__ void nv_convert(const NvFrags& fr, int d, const uint32_t (&ea)[4], const uint32_t (&eb)[4],
+                                           NvOps& o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o.a[i] = nv_operand((uint32_t)fr.a[i][d], ea[i]);
+        o.b[i] = nv_operand((uint32_t)fr.b[i][d], eb[i]);
+    }
+}
+
+// Substep H on fragments fr with scales sc: on entry o holds the operands
+// of dword 0; each dword's 16 products run while the next dword's operands
+// are decoded, the last while dword 0 of the next substep's fragments frn
+// (at substep HN, scales scn) is; on return o holds those.  One product,
+// then five decode instructions.
+template <int H, int HN>
+__device__ __forceinline__ void nv_substep(const NvFrags& fr, const NvScales& sc, const NvFrags& frn,
+                                           const NvScales& scn, NvOps& o, v16f (&acc)[4][4]) {
+    uint32_t ea0[4], ea1[4], eb0[4], eb1[4], na[4], nb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ea0[i] = nv_entry<H, 0>(sc.a[i]);
+        eb0[i] = nv_entry<H, 0>(sc.b[i]);
+        ea1[i] = nv_entry<H, 1>(sc.a[i]);
+        eb1[i] = nv_entry<H, 1>(sc.b[i]);
+        na[i] = nv_entry<HN, 0>(scn.a[i]);
+        nb[i] = nv_entry<HN, 0>(scn.b[i]);
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        v8h oa[4], ob[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            oa[i] = nv_operand((uint32_t)fr.a[i][d], ea[i][d >> 1]);
-            ob[i] = nv_operand((uint32_t)fr.b[i][d], eb[i][d >> 1]);
-        }
+        NvOps n;
+        if (d == 0) nv_convert(fr, 1, ea0, eb0, n);
+        else if (d == 1) nv_convert(fr, 2, ea1, eb1, n);
+        else if (d == 2) nv_convert(fr, 3, ea1, eb1, n);
+        else nv_convert(frn, 0, na, nb, n);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ob[j], oa[i], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.b[j], o.a[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+        }
+        o = n;
     }
 }
 
-// One step, staged as gemm_step (the same loads, reads and barrier), with
-// the fp16 products of each substep.
+// One step, staged as gemm_step (the same direct loads, fragment reads and
+// barrier), with the fp16 products of each substep.  o holds the operands
+// of dword 0 of substep 0 (decoded during the previous step).
 template <int S>
 __device__ __forceinline__ void nv_step(const GemmArgs& p, const GemmLane& L, const uint2* sa, const uint2* sb,
                                         int t, int wave, int lane, int wm, int wn, int64_t fa0, int64_t fb0,
-                                        NvScales& sc, GemmFrags& f0, v16f (&acc)[4][4]) {
-    GemmFrags f1;
+                                        NvScales& sc, const NvScales& sc_next, NvFrags& f0, NvOps& o,
+                                        v16f (&acc)[4][4]) {
+    NvFrags f1;
     gemm_issue_codes<S ^ 1, kHalfDma, kGemmDmaPerOperand>(L, min(t + 1, p.steps - 1), wave);
-    gemm_read<S>(f1, 1, lane, wm, wn);
-    nv_mfma<0>(f0, sc, acc);
-    gemm_read<S>(f0, 2, lane, wm, wn);
-    nv_mfma<1>(f1, sc, acc);
-    gemm_read<S>(f1, 3, lane, wm, wn);
-    nv_mfma<2>(f0, sc, acc);
+    nv_read<S>(f1, 1, lane, wm, wn);
+    nv_substep<0, 1>(f0, sc, f1, sc, o, acc);
+    nv_read<S>(f0, 2, lane, wm, wn);
+    nv_substep<1, 2>(f1, sc, f0, sc, o, acc);
+    nv_read<S>(f1, 3, lane, wm, wn);
+    nv_substep<2, 3>(f0, sc, f1, sc, o, acc);
     __builtin_amdgcn_sched_barrier(0);
     gemm_wait_barrier<0>();
     gemm_issue_codes<S, 0, kHalfDma>(L, min(t + 2, p.steps - 1), wave);
-    gemm_read<S ^ 1>(f0, 0, lane, wm, wn);
-    nv_mfma<3>(f1, sc, acc);
+    nv_read<S ^ 1>(f0, 0, lane, wm, wn);
+    nv_substep<3, 0>(f1, sc, f0, sc_next, o, acc);
     __builtin_amdgcn_sched_barrier(0);
     nv_issue_scales(p, sa, sb, min(t + 2, p.steps - 1), fa0, fb0, sc);
     __builtin_amdgcn_sched_barrier(0);
@@ -611,20 +657,32 @@ __global__ __launch_bounds__(256, 1) void k_nvfp4_gemm(NvGemmArgs q) {
     nv_issue_scales(p, sa, sb, min(1, nt - 1), fa0, fb0, s1);
     __builtin_amdgcn_sched_barrier(0);
     gemm_wait_barrier<kGemmDmaPerOperand + 8>();    // all but step 1's half and its 8 scale loads (also the table)
-    GemmFrags f0;
-    gemm_read<0>(f0, 0, lane, wm, wn);
+    NvFrags f0;
+    nv_read<0>(f0, 0, lane, wm, wn);
+    NvOps o;
+    {
+        uint32_t ea[4], eb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ea[i] = nv_entry<0, 0>(s0.a[i]);
+            eb[i] = nv_entry<0, 0>(s0.b[i]);
+        }
+        nv_convert(f0, 0, ea, eb, o);
+    }
+    // the step after the last reloads the last step (never used); its
+    // scales then are those of the last step, which the loads hold anyway
     if constexpr (PARITY == 1) {
-        nv_step<0>(p, L, sa, sb, 0, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
+        nv_step<0>(p, L, sa, sb, 0, wave, lane, wm, wn, fa0, fb0, s0, s1, f0, o, acc);
 #pragma unroll 1
         for (int t = 1; t < nt; t += 2) {
-            nv_step<1>(p, L, sa, sb, t, wave, lane, wm, wn, fa0, fb0, s1, f0, acc);
-            nv_step<0>(p, L, sa, sb, t + 1, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
+            nv_step<1>(p, L, sa, sb, t, wave, lane, wm, wn, fa0, fb0, s1, s0, f0, o, acc);
+            nv_step<0>(p, L, sa, sb, t + 1, wave, lane, wm, wn, fa0, fb0, s0, s1, f0, o, acc);
         }
     } else {
 #pragma unroll 1
         for (int t = 0; t < nt; t += 2) {
-            nv_step<0>(p, L, sa, sb, t, wave, lane, wm, wn, fa0, fb0, s0, f0, acc);
-            nv_step<1>(p, L, sa, sb, t + 1, wave, lane, wm, wn, fa0, fb0, s1, f0, acc);
+            nv_step<0>(p, L, sa, sb, t, wave, lane, wm, wn, fa0, fb0, s0, s1, f0, o, acc);
+            nv_step<1>(p, L, sa, sb, t + 1, wave, lane, wm, wn, fa0, fb0, s1, s0, f0, o, acc);
         }
     }
     gemm_wait_barrier<0>();
