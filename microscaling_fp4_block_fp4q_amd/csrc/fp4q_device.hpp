@@ -83,9 +83,10 @@ __device__ __forceinline__ float e4m3_value(uint32_t code) {
 // code, satfinite at 448 (0x7E).  v * 2^(3-e) is an exact scaling that puts
 // the three mantissa bits in front of the binary point (subnormals share
 // e = -6), rint rounds half-to-even, and a carry into the next binade falls
-// out of the code arithmetic.
+// out of the code arithmetic.  Saturation is a minimum (448 itself encodes
+// to 0x7E, and the minimum of a NaN and 448 is 448), so there is no branch.
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-    if (!(v < 448.0f)) return 0x7Eu;
+    v = fminf(v, 448.0f);
     int e = max((int)(as_u(v) >> 23) - 127, -6);
     float q = __builtin_ldexpf(v, 3 - e);
     float r = __builtin_rintf(q);
@@ -104,7 +105,7 @@ __device__ __forceinline__ float ue5m3_value(uint32_t code) {
 // code, saturating at 0xFE = 1.75 * 2^16; the same exact scaling and
 // half-to-even rint as e4m3_encode, with subnormals sharing e = -14.
 __device__ __forceinline__ uint32_t ue5m3_encode(float v) {
-    if (!(v < 114688.0f)) return 0xFEu;
+    v = fminf(v, 114688.0f);                       // saturation as in e4m3_encode
     int e = max((int)(as_u(v) >> 23) - 127, -14);
     float q = __builtin_ldexpf(v, 3 - e);
     float r = __builtin_rintf(q);

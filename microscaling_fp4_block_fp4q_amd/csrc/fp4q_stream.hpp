@@ -133,12 +133,13 @@ __device__ __forceinline__ void fill_scale_tab(ScaleTab& t, float g) {
 // (checked exhaustively around every grid point and midpoint of the 3-bit
 // mantissa scale formats).  Quotients below 2^-20 or above 2^20 round to the
 // smallest or the saturated code whatever their last bits, so the first
-// product stands for them (and keeps the residual clear of underflow).
+// product stands for them (and keeps the residual clear of underflow); the
+// refinement is computed either way and the choice is a select.
 __device__ __forceinline__ float block_quotient(float a, float d, float Rd) {
     const float q0 = a * Rd;
-    if (!(q0 >= 0x1p-20f && q0 <= 0x1p20f)) return q0;
     const float rr = __builtin_fmaf(-q0, d, a);
-    return __builtin_fmaf(rr, Rd, q0);
+    const float q1 = __builtin_fmaf(rr, Rd, q0);
+    return (q0 >= 0x1p-20f && q0 <= 0x1p20f) ? q1 : q0;
 }
 
 // Per-call constants of the scale choice.
@@ -329,6 +330,92 @@ __device__ __forceinline__ void quant_chunk(const float (&y)[E], const ScaleCtx&
     });
 }
 
+// The choice and encoding of quant_chunk for abs-max, prevent-zero and
+// 4-over-6 without a branch, for calls whose every candidate scale has a
+// division-free quotient (E8M0, or E4M3 / UE5M3 with g in the range that
+// keeps every table scale there: the usual case): the scale-code quotient
+// by its reciprocal refinement, the element quotient by the table's
+// reciprocal (0 for the zero scale; such a block holds finite values only),
+// saturation by a minimum.  A NaN block is encoded like any other here;
+// nanb reports it and fix_nan_blocks rewrites its outputs afterwards, so
+// the work of every chunk of a trip is one straight run of instructions
+// that the compiler can interleave.  Same results as quant_chunk.
+template <int SF, int ST, int B, int E>
+__device__ __forceinline__ void quant_chunk_fast(const float (&y)[E], const ScaleCtx& cx, int prevent_zero,
+                                                 uint32_t& cw, float (&p)[E], uint32_t (&sc)[(E + B - 1) / B],
+                                                 float (&sse)[(E + B - 1) / B], bool (&nanb)[(E + B - 1) / B]) {
+    static_assert(ST == ST_ABSMAX || ST == ST_FOUR_OVER_SIX, "scale choice from the block abs-max");
+    constexpr int BL = B < E ? B : E;
+    constexpr int LB = B / BL;
+    constexpr int NB = E / BL;
+    cw = 0;
+    static_for<NB>([&](auto bi) {
+        constexpr int b = decltype(bi)::value;
+        constexpr int OFF = b * BL;
+        uint32_t ab = 0;
+#pragma unroll
+        for (int i = 0; i < BL; ++i) ab = max(ab, as_u(y[OFF + i]) & 0x7FFFFFFFu);
+        ab = group_max_u32<LB>(ab);
+        const float a_b = as_f(ab);
+        nanb[b] = ab >= 0x7F800000u || !(cx.g < __builtin_inff());
+        uint32_t code;
+        float e;
+        if constexpr (SF == SF_E8M0) {
+            code = e8m0_absmax_code(ab);
+            e = group_tree_sum<LB>(
+                encode_hw<QM_E8M0, BL, OFF, false>(y, e8m0_value(code), e8m0_inverse(code), cw, p));
+        } else {
+            const uint32_t s6 = scale_encode<SF>(block_quotient(a_b, cx.six_g, cx.r6));
+            if constexpr (ST == ST_ABSMAX) {
+                code = (prevent_zero && s6 == 0u) ? 1u : s6;
+                const float2 sr = cx.tab->sr[code];
+                e = group_tree_sum<LB>(
+                    encode_hw<QM_FAST, BL, OFF, false>(y, sr.x, sr.x == 0.0f ? 0.0f : sr.y, cw, p));
+            } else {
+                const uint32_t s4 = scale_encode<SF>(block_quotient(a_b, cx.four_g, cx.r4));
+                const float2 sr6 = cx.tab->sr[s6], sr4 = cx.tab->sr[s4];
+                uint32_t cw6 = 0, cw4 = 0;
+                float p4[E];
+                const float e6 = group_tree_sum<LB>(
+                    encode_hw<QM_FAST, BL, OFF, false>(y, sr6.x, sr6.x == 0.0f ? 0.0f : sr6.y, cw6, p));
+                const float e4 = group_tree_sum<LB>(
+                    encode_hw<QM_FAST, BL, OFF, false>(y, sr4.x, sr4.x == 0.0f ? 0.0f : sr4.y, cw4, p4));
+                const bool take4 = e4 < e6;   // equal error keeps the smaller code s6
+                code = take4 ? s4 : s6;
+                e = take4 ? e4 : e6;
+                cw |= take4 ? cw4 : cw6;
+#pragma unroll
+                for (int i = 0; i < BL; ++i) p[OFF + i] = take4 ? p4[OFF + i] : p[OFF + i];
+            }
+        }
+        sc[b] = code;
+        sse[b] = e;
+    });
+}
+
+// The outputs of the NaN blocks of a chunk that quant_chunk_fast encoded as
+// numbers: the nibbles carry the sign only, the values are NaN with the
+// sign (the rotation's NaNs count as the positive quiet NaN), the error is
+// NaN and the scale the NaN code.
+template <int SF, int B, int E, bool ROT>
+__device__ __forceinline__ void fix_nan_blocks(const float (&y)[E], const bool (&nanb)[(E + B - 1) / B],
+                                               uint32_t& cw, float (&p)[E], uint32_t (&sc)[(E + B - 1) / B],
+                                               float (&sse)[(E + B - 1) / B]) {
+    constexpr int BL = B < E ? B : E;
+    constexpr int NB = E / BL;
+    static_for<NB>([&](auto bi) {
+        constexpr int b = decltype(bi)::value;
+        constexpr int OFF = b * BL;
+        constexpr uint32_t m = 4 * BL >= 32 ? 0xFFFFFFFFu : ((1u << (4 * BL)) - 1u) << (4 * OFF);
+        if (nanb[b]) {
+            cw &= ~m;
+            nan_block_hw<BL, OFF, ROT>(y, cw, p);
+            sse[b] = as_f(kQNaN);
+            sc[b] = scale_nan<SF>();
+        }
+    });
+}
+
 // Chunk index -> element offset in a [rows, ld] tensor with cpr chunks of E
 // values per row.
 template <int E>
@@ -478,6 +565,27 @@ __global__ __launch_bounds__(kThreads) void k_qstream(QuantArgs p) {
             }
         }
     };
+    // the outputs of chunk j
+    auto store_chunk = [&](int64_t j, uint32_t cw, const float (&dq)[E], const uint32_t (&sc)[NB],
+                           const float (&sse)[NB]) {
+        const int64_t e0 = j * E;                     // dense element index of the chunk
+        if (p.codes) store_code_word<E>(p.codes, e0, cw);
+        if (counting) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) atomicAdd(&bins[((cw >> (4 * i)) & 15u) * kThreads], 1u);
+        }
+        if (p.dq) store_dq_chunk<E>(p.dq, p.dq_dt, chunk_offset<E>(j, cpr, p.ld_dq, dq_contig), dq);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int64_t bi = e0 / B + b;
+            if constexpr (ST != ST_GIVEN) p.scales[bi] = (uint8_t)sc[b];
+            if (p.sse) p.sse[bi] = sse[b];
+            if (p.mse) {
+                const float m = sse[b] * (1.0f / (float)B);   // exact: B is a power of two
+                p.mse[bi] = (m == m) ? m : as_f(kQNaN);
+            }
+        }
+    };
     auto process = [&](const Trip& d, int64_t tt, auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
         const int64_t j0 = tt * per_trip + lane;
@@ -495,37 +603,72 @@ __global__ __launch_bounds__(kThreads) void k_qstream(QuantArgs p) {
             float dq[E], sse[NB];
             quant_chunk<SF, ST, B, E, (H > 0)>(y, cx, p.prevent_zero, given, cw, dq, sc, sse);
             if (!FULL && j >= nchunks) continue;
-            const int64_t e0 = j * E;                 // dense element index of the chunk
-            if (p.codes) store_code_word<E>(p.codes, e0, cw);
-            if (counting) {
-#pragma unroll
-                for (int i = 0; i < E; ++i) atomicAdd(&bins[((cw >> (4 * i)) & 15u) * kThreads], 1u);
-            }
-            if (p.dq) store_dq_chunk<E>(p.dq, p.dq_dt, chunk_offset<E>(j, cpr, p.ld_dq, dq_contig), dq);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int64_t bi = e0 / B + b;
-                if constexpr (ST != ST_GIVEN) p.scales[bi] = (uint8_t)sc[b];
-                if (p.sse) p.sse[bi] = sse[b];
-                if (p.mse) {
-                    const float m = sse[b] * (1.0f / (float)B);   // exact: B is a power of two
-                    p.mse[bi] = (m == m) ? m : as_f(kQNaN);
-                }
-            }
+            store_chunk(j, cw, dq, sc, sse);
         }
     };
-
-    int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave;
-    if (t < ntrips) {
-        Trip cur;
-        fetch(t, cur);
-        for (; t < nfull; t += tstride) {
-            Trip nxt;
-            fetch(t + tstride, nxt);
-            process(cur, t, IC<1>{});
-            cur = nxt;
+    // every chunk of the trip through quant_chunk_fast, then the NaN blocks
+    // (rare: one wave-level test; their values are widened and rotated
+    // again from the loaded words), then the stores
+    auto process_fast = [&](const Trip& d, int64_t tt, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        const int64_t j0 = tt * per_trip + lane;
+        float dq[R][E], sse[R][NB];
+        uint32_t cw[R], sc[R][NB];
+        bool nb[R][NB];
+        bool any_nan = false;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            float y[E];
+            widen_chunk<InT, E>(d.raw[k], y);
+            if constexpr (H > 0) fwht_chunk<H, E>(y, lane);
+            if constexpr (ST == ST_ABSMAX || ST == ST_FOUR_OVER_SIX)
+                quant_chunk_fast<SF, ST, B, E>(y, cx, p.prevent_zero, cw[k], dq[k], sc[k], sse[k], nb[k]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) any_nan |= nb[k][b];
         }
-        if (t < ntrips) process(cur, t, IC<0>{});     // the last, partial trip
+        if (any_nan) {
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                float y[E];
+                widen_chunk<InT, E>(d.raw[k], y);
+                if constexpr (H > 0) fwht_chunk<H, E>(y, lane);
+                fix_nan_blocks<SF, B, E, (H > 0)>(y, nb[k], cw[k], dq[k], sc[k], sse[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int64_t j = j0 + k * kTileUnits;
+            if (!FULL && j >= nchunks) continue;
+            store_chunk(j, cw[k], dq[k], sc[k], sse[k]);
+        }
+    };
+    auto run = [&](auto& proc) {
+        int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+        if (t < ntrips) {
+            Trip cur;
+            fetch(t, cur);
+            for (; t < nfull; t += tstride) {
+                Trip nxt;
+                fetch(t + tstride, nxt);
+                proc(cur, t, IC<1>{});
+                cur = nxt;
+            }
+            if (t < ntrips) proc(cur, t, IC<0>{});    // the last, partial trip
+        }
+    };
+    // the branch-free path serves abs-max, prevent-zero and 4-over-6 when
+    // every candidate scale has a division-free quotient (16-bit inputs with
+    // the 32-point rotation keep the chunk-by-chunk path: there the larger
+    // register footprint of the interleaved trip measured 5-8 % slower)
+    if constexpr ((ST == ST_ABSMAX || ST == ST_FOUR_OVER_SIX) && !(ES == 2 && H == 32)) {
+        bool fast = true;
+        if constexpr (SF != SF_E8M0)
+            fast = cx.div_fast && fast_quotient_range(scale_value<SF>(1u) * g) &&
+                   fast_quotient_range(scale_value<SF>(scale_top<SF>()) * g);
+        if (fast) run(process_fast);
+        else run(process);
+    } else {
+        run(process);
     }
     if (counting) {
         // thread t gathers code t & 15 from the 16 threads of its group of 16
