@@ -21,10 +21,12 @@ one call to the next).
 All inputs are generated once and are resident in HBM before timing; every
 output buffer is preallocated; the timed region holds only library calls.
 value = algorithmic bytes of the step (each input read once, each output
-written once) / step time.  Per-call HIP events over the timed steps give
-the per-strategy rates and the roofline of the dominant kernel.  A cold
-leg times every call once more with the caches flushed before it (1 GiB of
-reads and writes on the same stream, outside the events).
+written once) / step time.  Inside the timed steps HIP events bracket only
+the launches of the dominant kernel family (found in the warm-up), whose
+live launch times give the roofline; the per-strategy rates come from the
+same steps run again afterwards with every call bracketed by events.  A
+cold leg times every call once more with the caches flushed before it
+(1 GiB of reads on the same stream, outside the events).
 
 Beside the step, the other workloads are timed per call, warm and cold:
 fp32 1024 x 1024 (launch-bound, reported only), the Llama-3.1-8B-shaped
@@ -1054,9 +1056,11 @@ def main():
         print("[bench] profiling run done", file=sys.stderr, flush=True)
         return
 
-    def step(record=False):
+    def step(record=None):
+        """One pass over the calls; record = None (no events), "all", or
+        the ids of the calls to bracket with HIP events."""
         for c in calls:
-            if record:
+            if record is not None and (record == "all" or id(c) in record):
                 e0, e1 = events(torch)
                 e0.record()
                 c()
@@ -1065,25 +1069,49 @@ def main():
             else:
                 c()
 
-    print(f"[bench] {len(calls)} calls per step, warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def family(c):
+        return (c.meta.get("strategy", c.kind), c.meta.get("B"))
 
-    # timed region: K steps bracketed by device synchronisation
+    def mean_ms(c):
+        return float(np.mean([a.elapsed_time(b) for a, b in c.times]))
+
+    # Warm-up.  Its last step (an extra untimed step with --warmup 0) brackets
+    # every call with events to find the dominant kernel family: the
+    # (strategy, block) family with the largest share of the step.
+    print(f"[bench] {len(calls)} calls per step, warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(max(args.warmup - 1, 0)):
+        step()
+    step(record="all")
+    torch.cuda.synchronize()
+    fam_ms = {}
+    for c in calls:
+        fam_ms[family(c)] = fam_ms.get(family(c), 0.0) + mean_ms(c)
+        c.times = []
+    dom_key = max(fam_ms, key=fam_ms.get)
+    dom_ids = {id(c) for c in calls if family(c) == dom_key}
+
+    # Timed region: K steps bracketed by device synchronisation.  Events
+    # bracket only the dominant family's launches (the roofline's live
+    # launch times): an event pair around every call adds about 1 ms to a
+    # 7 ms step (measured), which is measurement, not work.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(record=True)
+        step(record=dom_ids)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
-
-    per_call = []
+    dom_live = {id(c): mean_ms(c) for c in calls if id(c) in dom_ids}
     for c in calls:
-        ms = float(np.mean([a.elapsed_time(b) for a, b in c.times]))
-        per_call.append((c, ms))
+        c.times = []
+
+    # Per-call times for the per-strategy table: the same steps again after
+    # the timed region, every call bracketed by events.
+    for _ in range(args.steps):
+        step(record="all")
+    torch.cuda.synchronize()
+    per_call = [(c, mean_ms(c)) for c in calls]
 
     # cold leg: every call once more, each after a cache flush outside its events
     flush = Flusher(torch, dev)
@@ -1112,13 +1140,8 @@ def main():
                      "GB/s_cold": round(b / (cms * 1e6), 1), "hbm_frac_cold": round(b / (cms * 1e6) / HBM_PEAK_GBS, 4)}
                  for k, (b, e, ms, cms) in groups.items()}
 
-    # dominant kernel: the kernel family (strategy, block) with the largest share of the step
-    fam = {}
-    for c, ms in per_call:
-        key = (c.meta.get("strategy", c.kind), c.meta.get("B"))
-        fam.setdefault(key, []).append((c, ms))
-    dom_key = max(fam, key=lambda k: sum(ms for _, ms in fam[k]))
-    dom = fam[dom_key]
+    # dominant kernel family (found in the warm-up) with its launch times from the timed region
+    dom = [(c, dom_live[id(c)]) for c in calls if id(c) in dom_ids]
     strategy, B = dom_key
     vprobe = valu_probe_summary()
     if strategy == "brute-force":
