@@ -202,3 +202,27 @@ def test_brute_force_extreme_global_scale(O_lib, g, xs, B):
     gpu = gpu_quantize(x, S.F32, cfg)
     ref = oracle_quantize(x, S.F32, cfg)
     compare_quant(gpu, ref)
+
+
+@pytest.mark.parametrize("g,xs", [(2.0 ** -110, 2.0 ** -104), (2.0 ** -63, 2.0 ** -57), (2.0 ** -62, 2.0 ** -56),
+                                  (2.0 ** 57, 2.0 ** 63), (2.0 ** 59, 2.0 ** 65), (1.0e33, 5.0e34)])
+@pytest.mark.parametrize("strategy", [F.ABSMAX, F.PREVENT_ZERO, F.FOUR_OVER_SIX])
+@pytest.mark.parametrize("B", [4, 16, 32])
+def test_streaming_extreme_global_scale(O_lib, g, xs, strategy, B):
+    """User scales on both sides of the range that the branch-free trips
+    need (fl(6 g) and fl(4 g) in [2^-60, 2^60], every table scale
+    fl(dec(c) g) in [2^-100, 2^100]): g = 2^-62 and 2^57 take the
+    branch-free trips, 2^-63, 2^59, 2^-110 and 1e33 the chunk-by-chunk path
+    (with the IEEE division where a quotient leaves its range).  Values near
+    g times mid-range codes, with a NaN, infinities and a zero block in whole
+    trips (64 rows of 512 values)."""
+    x = (S.laplace(64, 512, 41) * np.float32(xs)).astype(np.float32)
+    x[3, 17] = np.nan
+    x[40, 200] = np.inf
+    x[63, 511] = -np.inf
+    x[10, :16] = 0.0
+    cfg = F.config(E4M3, B, strategy, F.GLOBAL_USER, g)
+    note(f"streaming strategy={strategy} B={B} g={g} x scale={xs}")
+    gpu = gpu_quantize(x, S.F32, cfg)
+    ref = oracle_quantize(x, S.F32, cfg)
+    compare_quant(gpu, ref)
