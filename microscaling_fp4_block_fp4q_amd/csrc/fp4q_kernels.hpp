@@ -752,18 +752,33 @@ struct DqSink {
     void* out;           // global output, or null
     int64_t off;         // element offset of the unit in out
     int dt;
+    bool direct;         // contiguous fp32 units of 4: one streaming 16-byte store per lane
     __device__ __forceinline__ void operator()(int o, const float (&v)[4]) const {
-        if (slot) store_elems_rt<4>(slot, dt, o, v);
-        else if (out) store_elems_rt<4>(out, dt, off + o, v);
+        if (slot) {
+            store_elems_rt<4>(slot, dt, o, v);
+        } else if (out) {
+            if (direct) store_stream_f32<4>(reinterpret_cast<float*>(out) + off + o, v);
+            else store_elems_rt<4>(out, dt, off + o, v);
+        }
     }
 };
 
+// Contiguous tensors whose unit is exactly 16 bytes need no LDS exchange:
+// lane l's unit is already the l-th 16-byte piece of the tile.  For the
+// input that holds for units of 4 fp32 or 8 16-bit values, for the fp32
+// dequantized output for units of 4.
+template <class InT, int U>
+constexpr bool bf_direct_input() { return U * ElemSize<InT>::value == 16; }
+template <int U, class P>
+__device__ __forceinline__ bool bf_direct_dq(const P& p) { return U == 4 && p.contiguous && p.dq_dt == DT_F32; }
+
 template <int U, class P>
 __device__ __forceinline__ DqSink<U> dq_sink(const P& p, char* lds, int lane, int64_t u, bool active) {
-    if (!p.dq) return {nullptr, nullptr, 0, 0};
-    if (p.contiguous) return {lds + lane * slot_bytes<U>(), nullptr, 0, p.dq_dt};
-    if (!active) return {nullptr, nullptr, 0, 0};
-    return {nullptr, p.dq, unit_offset<U>(u, p.units_per_row, p.ld_dq, false), p.dq_dt};
+    if (!p.dq) return {nullptr, nullptr, 0, 0, false};
+    const bool direct = bf_direct_dq<U>(p);
+    if (p.contiguous && !direct) return {lds + lane * slot_bytes<U>(), nullptr, 0, p.dq_dt, false};
+    if (!active) return {nullptr, nullptr, 0, 0, false};
+    return {nullptr, p.dq, unit_offset<U>(u, p.units_per_row, p.ld_dq, p.contiguous), p.dq_dt, direct};
 }
 
 // ---------------------------------------------------------------------------
@@ -881,7 +896,7 @@ __device__ __forceinline__ void store_unit_outputs(const QuantArgs& p, int64_t u
             store_stream_f32<NB>(p.mse + u * NB, m);
         }
     }
-    if (p.dq && p.contiguous) {
+    if (p.dq && p.contiguous && !bf_direct_dq<U>(p)) {
         const int eo = p.dq_dt == DT_F32 ? 4 : 2;
         tile_flush<U>(reinterpret_cast<char*>(p.dq) + u0 * U * eo, p.dq_dt, nvalid, lds, lane);
     }
@@ -1394,17 +1409,18 @@ __device__ __forceinline__ float bf_block_sse(const float (&y)[U], uint32_t c, c
 }
 
 // Tile load for the brute-force kernels: contiguous tensors through the
-// wave's LDS slots, strided ones unit by unit; rotated when H != 0; idle
-// lanes hold zeros (they contribute empty windows).
+// wave's LDS slots (units of 16 bytes straight into the lanes), strided
+// ones unit by unit; rotated when H != 0; idle lanes hold zeros (they
+// contribute empty windows).
 template <class InT, int U, int H, class P>
 __device__ __forceinline__ void bf_load_tile(const P& p, int64_t u0, int nvalid, int lane, char* lds, float (&y)[U]) {
     const InT* x = reinterpret_cast<const InT*>(p.x);
     const int64_t u = u0 + lane;
     const bool active = lane < nvalid;
-    if (p.contiguous) {
+    if (p.contiguous && !bf_direct_input<InT, U>()) {
         tile_load<InT, U>(x + u0 * U, nvalid, lds, lane, y);
     } else if (active) {
-        load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, false), y);
+        load_elems<InT, U>(x + unit_offset<U>(u, p.units_per_row, p.ld_x, p.contiguous), y);
     } else {
 #pragma unroll
         for (int i = 0; i < U; ++i) y[i] = 0.0f;
